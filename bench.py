@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: the KV scatter of the
+step's new rows (store_kv) followed by paged decode attention, on the
+Llama-3.2-1B-shaped decode batch (64 requests, 32 query / 8 KV heads,
+head_dim 64, page_size 16, seq_lens uniform in [128, 2048]).  The batch is
+replicated R times in HBM and the steps rotate over the replicas, so the
+timed working set (>= 1 GiB) cannot stay in the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  ``value`` is algorithmic bytes per step (K/V read
+once per KV head, q, out, page table, seq_lens, plus store_kv's reads and
+writes) over wall-clock time per step.  ``roofline`` is for the decode
+kernel alone, timed with HIP events on its launch stream.  ``also`` holds
+the same measurement for the other workloads: Qwen3-0.6B-shaped decode,
+long-context decode, and chunked prefill (TFLOP/s against the bf16 MFMA
+peak).  ``cpu_baseline`` is the float64 CPU oracle on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+MIN_WORKING_SET = 1 << 30
+METRIC = "paged decode attn HBM GB/s (% peak) + causal prefill attn TFLOP/s (% peak)"
+PRIMARY = "llama_decode"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- algorithmic work --------------------------------------------------------
+
+def decode_bytes(w) -> int:
+    n = w.seq_lens_np.astype(np.int64)
+    ps = w.page_size
+    kv = int(n.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * 2
+    meta = int(((n + ps - 1) // ps).sum()) * 4 + 4 * w.num_seqs
+    return kv + qo + meta
+
+
+def store_bytes(w) -> int:
+    if w.k_new is None:
+        return 0
+    T = w.k_new.shape[0]
+    return 2 * T * w.num_kv_heads * w.head_dim * 2 * 2 + 4 * T
+
+
+def prefill_flops(w) -> int:
+    L = w.q_lens_np.astype(np.int64)
+    P = w.prefix_lens_np.astype(np.int64)
+    pairs = int((L * P + L * (L + 1) // 2).sum())
+    return 4 * w.head_dim * w.num_q_heads * pairs
+
+
+def prefill_bytes(w) -> int:
+    n = w.seq_lens_np.astype(np.int64)
+    kv = int(n.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = 2 * w.num_tokens * w.num_q_heads * w.head_dim * 2
+    return kv + qo
+
+
+# ---- GPU timing ----------------------------------------------------------------
+
+def _replicate(w, R):
+    import copy
+
+    reps = [w]
+    for _ in range(R - 1):
+        c = copy.copy(w)
+        for f in ("q", "k_cache", "v_cache", "page_table", "seq_lens", "prefix_lens",
+                  "cu_seqlens_q", "k_new", "v_new", "out_loc"):
+            t = getattr(w, f)
+            setattr(c, f, None if t is None else t.clone())
+        reps.append(c)
+    return reps
+
+
+def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0):
+    import torch
+
+    import paged_kv_attention_out_amd as pkv
+    from paged_kv_attention_out_amd import inputs
+
+    lib = pkv.lib()
+    w = inputs.make_workload(name, device="cuda", poison=False)
+    is_decode = w.kind == "decode"
+    work_bytes = decode_bytes(w) if is_decode else prefill_bytes(w)
+    R = max(1, min(64, math.ceil(MIN_WORKING_SET / max(work_bytes, 1))))
+    reps = _replicate(w, R)
+    stream = torch.cuda.current_stream().cuda_stream
+    B, Hq, Hkv, d, ps = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
+    split = pkv.pkv_decode_split_tokens(B, Hkv, w.max_seq_len, split_tokens) if is_decode else 0
+    ws = pkv.decode_workspace(B, Hq, Hkv, d, w.max_seq_len, split_tokens) if is_decode else None
+    ws_ptr, ws_bytes = (0, 0) if ws is None else (ws.data_ptr(), ws.numel())
+
+    # Pre-marshalled C calls: the timed loop only enqueues.
+    calls = []
+    for c in reps:
+        out = torch.empty_like(c.q)
+        st = None
+        if c.k_new is not None:
+            st = (c.k_new.data_ptr(), c.v_new.data_ptr(), c.out_loc.data_ptr(),
+                  c.k_new.shape[0], c.k_cache.data_ptr(), c.v_cache.data_ptr(),
+                  c.k_cache.shape[0] * ps, Hkv, d, stream)
+        if is_decode:
+            at = (c.q.data_ptr(), c.k_cache.data_ptr(), c.v_cache.data_ptr(), ps, c.num_pages,
+                  c.page_table.data_ptr(), c.page_table.shape[1], c.seq_lens.data_ptr(), B,
+                  w.max_seq_len, Hq, Hkv, d, w.scale, split_tokens, out.data_ptr(), ws_ptr,
+                  ws_bytes, stream)
+        else:
+            at = (c.q.data_ptr(), c.cu_seqlens_q.data_ptr(), c.prefix_lens.data_ptr(), B,
+                  w.num_tokens, w.max_q_len, w.max_seq_len, c.k_cache.data_ptr(),
+                  c.v_cache.data_ptr(), ps, c.num_pages, c.page_table.data_ptr(),
+                  c.page_table.shape[1], Hq, Hkv, d, w.scale, out.data_ptr(), stream)
+        calls.append((st, at, out))
+    f_store = lib.pkv_store_kv
+    f_attn = lib.pkv_paged_attn_decode if is_decode else lib.pkv_paged_attn_prefill
+
+    def step(i, ev=None):
+        st, at, _ = calls[i % R]
+        if st is not None and f_store(*st) != 0:
+            raise RuntimeError("pkv_store_kv failed")
+        if ev is not None:
+            ev[0].record()
+        if f_attn(*at) != 0:
+            raise RuntimeError("attention call failed")
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = [a.elapsed_time(b) for a, b in events]
+    for _, _, out in calls:
+        if not torch.isfinite(out.float()).all():
+            raise RuntimeError(f"{name}: non-finite output")
+    if R > 1 and not torch.equal(calls[0][2], calls[1][2]):
+        raise RuntimeError(f"{name}: replicas disagree")
+    res = dict(workload=w, replicas=R, split=split, ms_per_step=(t1 - t0) * 1e3 / steps,
+               kernel_ms_mean=float(np.mean(kernel_ms)), kernel_ms_median=float(np.median(kernel_ms)),
+               kernel_ms_min=float(np.min(kernel_ms)))
+    return res
+
+
+# ---- CPU baseline (the oracle) ------------------------------------------------
+
+def cpu_baseline(name: str, budget_s: float):
+    """Oracle store + decode over whole passes of the batch, until budget_s."""
+    import torch
+
+    from oracle import paged_attention as orc
+    from paged_kv_attention_out_amd import inputs
+
+    w = inputs.make_workload(name, device="cuda", poison=False)
+    kc, vc = inputs.bf16_bits(w.k_cache), inputs.bf16_bits(w.v_cache)
+    q = inputs.bf16_bits(w.q)
+    kn = None if w.k_new is None else inputs.bf16_bits(w.k_new)
+    vn = None if w.v_new is None else inputs.bf16_bits(w.v_new)
+    del w.k_cache, w.v_cache
+    torch.cuda.empty_cache()
+    nbytes = decode_bytes(w) + store_bytes(w)
+    passes, done_bytes = 0, 0
+    c0, t0 = time.process_time(), time.perf_counter()
+    while True:
+        if kn is not None:
+            kc2, vc2 = orc.store_kv(kc, vc, kn, vn, w.out_loc_np)
+        else:
+            kc2, vc2 = kc, vc
+        orc.decode(q, kc2, vc2, w.page_table_np, w.seq_lens_np, w.scale)
+        passes += 1
+        done_bytes += nbytes
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s",
+            "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) of store_kv + decode over the {name} batch "
+                      f"(float64 NumPy, {len(os.sched_getaffinity(0))} host cores available); "
+                      f"{wall:.1f} s"}
+
+
+# ---- main ------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=PRIMARY)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_attention_out_amd as pkv
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} CUs={props.multi_processor_count} "
+        f"arch={getattr(props, 'gcnArchName', '?')} lib={pkv.version()}")
+
+    r = time_workload(args.workload, args.steps, args.warmup, args.split_tokens)
+    w = r["workload"]
+    if w.kind != "decode":
+        raise SystemExit("the primary line is a decode workload")
+    step_bytes = decode_bytes(w) + store_bytes(w)
+    value = step_bytes / (r["ms_per_step"] * 1e-3) / 1e9
+    achieved = decode_bytes(w) / (r["kernel_ms_mean"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "num_seqs": w.num_seqs,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "page_size": w.page_size,
+                   "seq_lens_sum": int(w.seq_lens_np.sum()), "seed": w.seed,
+                   "replicas": r["replicas"], "split_tokens": r["split"],
+                   "step": "store_kv + paged decode", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "decode_kernel",
+                     "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 2),
+                     "kernel_us_median": round(r["kernel_ms_median"] * 1e3, 2),
+                     "bytes_per_launch": decode_bytes(w)},
+    }
+    if not args.no_also:
+        also = {}
+        for name in ("qwen_decode", "long_decode", "chunked_prefill"):
+            torch.cuda.empty_cache()
+            steps = max(10, args.steps // 10)
+            a = time_workload(name, steps, max(3, args.warmup // 4))
+            wa = a["workload"]
+            if wa.kind == "decode":
+                gbs = decode_bytes(wa) / (a["kernel_ms_mean"] * 1e-3) / 1e9
+                also[name] = {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "kernel_us_mean": round(a["kernel_ms_mean"] * 1e3, 2),
+                              "ms_per_step": round(a["ms_per_step"], 4),
+                              "tokens_per_s": round(wa.num_seqs / (a["ms_per_step"] * 1e-3), 1),
+                              "split_tokens": a["split"], "replicas": a["replicas"]}
+            else:
+                tf = prefill_flops(wa) / (a["kernel_ms_mean"] * 1e-3) / 1e12
+                also[name] = {"TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                              "kernel_us_mean": round(a["kernel_ms_mean"] * 1e3, 2),
+                              "ms_per_step": round(a["ms_per_step"], 4),
+                              "tokens_per_s": round(wa.num_tokens / (a["ms_per_step"] * 1e-3), 1),
+                              "flops": prefill_flops(wa), "replicas": a["replicas"]}
+            del a, wa
+        line["also"] = also
+        line["tokens_per_s"] = round(w.num_seqs / (r["ms_per_step"] * 1e-3), 1)
+    if not args.no_cpu_baseline:
+        del r, w
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

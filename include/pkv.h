@@ -1,0 +1,200 @@
+/*
+ * pkv.h -- attention over a paged KV cache on AMD MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Plain pointers and sizes only.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer (memory from hipMalloc or a
+ *   framework allocator on the current device) and must be 16-byte aligned.
+ *   The caller owns every buffer; the library allocates nothing and keeps
+ *   no per-call state.
+ * - Element types: K/V/q/out are bfloat16 stored as 16-bit words; every
+ *   index array is int32.  All tensors are dense and row-major in the shape
+ *   given.
+ * - KV pool layout (miniVLLM "Engine Architecture", allocate_kv_cache: one
+ *   tensor per layer and per K/V of shape [num_blocks, block_size,
+ *   num_kv_heads, head_dim]): k_cache and v_cache are each
+ *   [num_pages, page_size, num_kv_heads, head_dim].  The "slot" of a token is
+ *   its row in the flat [num_pages * page_size, num_kv_heads, head_dim] view:
+ *   slot = page * page_size + offset_in_page.
+ * - Page table (mini-sglang "Engine Class", Key Attributes: page_table;
+ *   miniVLLM prepare_prefill / prepare_decode: block_tables): int32
+ *   [num_seqs, page_table_stride]; entry [r, j] is the physical page holding
+ *   logical positions j*page_size .. (j+1)*page_size-1 of request r.  Entries
+ *   past a request's last page are never read.
+ * - GQA (miniVLLM "LLMEngine", Config parameters: num_heads, num_kv_heads):
+ *   query head h reads K/V head h / (num_q_heads / num_kv_heads).
+ * - stream: a hipStream_t (NULL = the legacy default stream).  Work is
+ *   enqueued asynchronously; no entry point synchronises the host.
+ * - Errors: a non-zero status is returned BEFORE anything is enqueued when
+ *   an argument the host can check is wrong; PKV_EHIP reports a launch
+ *   failure.  Device-resident values (page ids, slots, lengths) are not
+ *   checked on the host: out-of-range values are clamped or skipped inside
+ *   the kernels so no access leaves the buffers described here, and the
+ *   affected outputs are unspecified.
+ * - Thread safety: calls may be made from any host thread; calls that share
+ *   an output or workspace buffer must be ordered by the caller.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_EINVAL 1        /* null pointer, bad size, misaligned pointer,  */
+                            /* inconsistent shapes                          */
+#define PKV_EUNSUPPORTED 2  /* legal but not built: head_dim, page_size or  */
+                            /* query-heads-per-KV-head outside the kernels  */
+#define PKV_ENOSPACE 3      /* workspace smaller than required              */
+#define PKV_EHIP 4          /* the HIP runtime failed to launch a kernel    */
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* pkv_strerror(int status);
+
+/* Library version string, e.g. "pkv 0.1.0 gfx950". */
+const char* pkv_version(void);
+
+/*
+ * pkv_store_kv -- scatter this step's new K/V rows into the pool.
+ *
+ * For t in [0, num_tokens): row out_loc[t] of the flat K pool receives
+ * k_new[t] and row out_loc[t] of the flat V pool receives v_new[t]; nothing
+ * else in the pools changes.  This is the write that "out_loc" names in
+ * mini-sglang "Engine Class" (forward_batch) and "slot_mapping" names in
+ * miniVLLM "Engine Architecture" (prepare_prefill / prepare_decode); prefill
+ * writes the initial KV cache and decode appends to it (zero-to-sglang Ch.1,
+ * section 3.2).  The copy is bit-exact.
+ *
+ *   k_new, v_new : [num_tokens, num_kv_heads, head_dim] bf16, read only
+ *   out_loc      : [num_tokens] int32 slots; must be distinct (several
+ *                  tokens writing one slot leave one of them, unspecified);
+ *                  a slot outside [0, num_slots) is skipped
+ *   k_cache,
+ *   v_cache      : pools, num_slots = num_pages * page_size rows of
+ *                  num_kv_heads * head_dim values; written in place
+ *   head_dim     : any multiple of 8 (rows are moved in 16-byte pieces)
+ *
+ * num_tokens == 0 is a no-op returning PKV_OK.
+ */
+int pkv_store_kv(const void* k_new, const void* v_new, const int32_t* out_loc,
+                 int64_t num_tokens, void* k_cache, void* v_cache,
+                 int64_t num_slots, int32_t num_kv_heads, int32_t head_dim,
+                 void* stream);
+
+/*
+ * pkv_decode_workspace_bytes -- size of the workspace pkv_paged_attn_decode
+ * needs for these arguments (0 when every request fits one split).  Pass the
+ * same split_tokens (0 = automatic) as to the decode call.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int32_t split_tokens);
+
+/*
+ * pkv_decode_split_tokens -- the split length (tokens per split) that
+ * pkv_paged_attn_decode uses for these arguments; split_tokens != 0 is
+ * returned rounded as the call would use it.  0 on invalid arguments.
+ */
+int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t max_seq_len, int32_t split_tokens);
+
+/*
+ * pkv_paged_attn_decode -- one query token per request attends to all of
+ * its context through the page table.
+ *
+ * Decode feeds exactly one new token per sequence; context_lens counts
+ * every token processed so far and block_tables give the KV history
+ * (miniVLLM "Engine Architecture", prepare_decode).  seq_lens[r] therefore
+ * INCLUDES the current token, whose K/V row must already be in the pool
+ * (store first with pkv_store_kv).  For every query head h:
+ *
+ *   out[r, h, :] = softmax_j( softmax_scale * <q[r,h], K[r, j, h/g]> ) V[r, j, h/g]
+ *
+ * over j = 0 .. seq_lens[r]-1, with K[r, j, kvh] the row of slot
+ * page_table[r, j / page_size] * page_size + j % page_size.  Long contexts
+ * are cut into splits of split_tokens tokens that run in parallel and are
+ * merged in the same launch (flash-decoding).
+ *
+ *   q            : [num_seqs, num_q_heads, head_dim] bf16
+ *   k_cache,
+ *   v_cache      : [num_pages, page_size, num_kv_heads, head_dim] bf16
+ *   page_table   : [num_seqs, page_table_stride] int32
+ *   seq_lens     : [num_seqs] int32, 1 <= seq_lens[r] <= max_seq_len;
+ *                  a request with seq_lens[r] <= 0 gets an all-zero output
+ *   max_seq_len  : host upper bound of seq_lens (sizes the launch);
+ *                  page_table_stride * page_size >= max_seq_len
+ *   head_dim     : 64 or 128
+ *   page_size    : 16, 32, 64, 128 or 256
+ *   num_q_heads / num_kv_heads : 1, 2 or 4
+ *   softmax_scale: finite and > 0 (typically 1/sqrt(head_dim))
+ *   split_tokens : 0 = automatic, else a multiple of 16 in [16, 65536]
+ *   out          : [num_seqs, num_q_heads, head_dim] bf16 (round to nearest even)
+ *   workspace    : device buffer of at least pkv_decode_workspace_bytes(...)
+ *                  bytes, 256-byte aligned, ZERO-FILLED before its first use;
+ *                  every call returns its counter words to zero, so one
+ *                  buffer serves any sequence of calls ordered on a stream.
+ *                  May be NULL when the required size is 0.
+ */
+int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          int32_t page_size, int64_t num_pages,
+                          const int32_t* page_table, int32_t page_table_stride,
+                          const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t max_seq_len, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          float softmax_scale, int32_t split_tokens, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_attn_prefill -- causal attention of a flat ragged batch of new
+ * tokens over their cached prefix and themselves.
+ *
+ * Prefill feeds only the tokens after each request's cached prefix, laid
+ * out flat with cumulative offsets cu_seqlens_q, e.g. [0, 5, 8, 12]
+ * (miniVLLM "Engine Architecture", prepare_prefill); the extend length is
+ * the sequence length minus the cached length (zero-to-sglang Ch.1,
+ * section 3.3).  New token i of request r sits at absolute position
+ * prefix_lens[r] + i and sees keys 0 .. prefix_lens[r] + i of its request:
+ *
+ *   out[t, h, :] = softmax_{j <= P_r+i}( softmax_scale * <q[t,h], K[r,j,h/g]> ) V[r, j, h/g]
+ *
+ * with t = cu_seqlens_q[r] + i.  Keys are read through the page table, so
+ * the new tokens' K/V rows must already be in the pool (pkv_store_kv first).
+ *
+ *   q            : [num_tokens, num_q_heads, head_dim] bf16
+ *   cu_seqlens_q : [num_seqs + 1] int32, non-decreasing, cu[0] = 0,
+ *                  cu[num_seqs] = num_tokens; request r owns rows
+ *                  cu[r] .. cu[r+1]-1 (an empty request is allowed)
+ *   prefix_lens  : [num_seqs] int32 >= 0, cached tokens per request
+ *   max_q_len    : host upper bound of cu[r+1]-cu[r] (sizes the launch)
+ *   max_seq_len  : host upper bound of prefix_lens[r] + (cu[r+1]-cu[r]);
+ *                  page_table_stride * page_size >= max_seq_len
+ *   head_dim     : 64 or 128
+ *   page_size    : 16, 32, 64, 128 or 256
+ *   num_q_heads / num_kv_heads : 1, 2, 4 or 8
+ *   softmax_scale: finite and > 0
+ *   out          : [num_tokens, num_q_heads, head_dim] bf16; rows outside
+ *                  every request are not written
+ *
+ * num_tokens == 0 is a no-op returning PKV_OK.
+ */
+int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q,
+                           const int32_t* prefix_lens, int32_t num_seqs,
+                           int32_t num_tokens, int32_t max_q_len,
+                           int32_t max_seq_len, const void* k_cache,
+                           const void* v_cache, int32_t page_size,
+                           int64_t num_pages, const int32_t* page_table,
+                           int32_t page_table_stride, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           float softmax_scale, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -170,9 +170,9 @@ def prefill(q: np.ndarray, cu_seqlens_q: np.ndarray, prefix_lens: np.ndarray,
 
 def prefill_dense(q: np.ndarray, cu_seqlens_q: np.ndarray, prefix_lens: np.ndarray,
                   k_cache: np.ndarray, v_cache: np.ndarray, page_table: np.ndarray,
-                  scale: float) -> np.ndarray:
-    """Same result as ``prefill`` for all rows, computed one [L, n] score
-    block per (request, head) instead of row by row (faster on big inputs)."""
+                  scale: float, heads: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Same result as ``prefill`` for all rows of the given heads, computed
+    one [L, n] score block per (request, head) instead of row by row."""
     T, Hq, d = q.shape
     Hkv = k_cache.shape[2]
     out = np.full((T, Hq, d), np.nan)
@@ -185,7 +185,7 @@ def prefill_dense(q: np.ndarray, cu_seqlens_q: np.ndarray, prefix_lens: np.ndarr
         kr = gather(k_cache, page_table[r], P + L)
         vr = gather(v_cache, page_table[r], P + L)
         qr = bf16_to_f64(q[s0:s1])
-        for h in range(Hq):
+        for h in (range(Hq) if heads is None else heads):
             kvh = kv_head_of(h, Hq, Hkv)
             out[s0:s1, h] = attend(qr[:, h], kr[:, kvh], vr[:, kvh], P, scale)
     return out

@@ -1,0 +1,19 @@
+"""Attention over a paged KV cache for AMD MI355X (gfx950).
+
+The compute lives in libpkv.so (HIP kernels behind the C ABI of
+include/pkv.h); this package holds its build script, a thin ctypes binding
+and the seeded input generators used by the tests and the benchmark.
+"""
+
+from ._lib import (  # noqa: F401
+    PKVError,
+    decode_workspace,
+    lib,
+    pkv_decode_split_tokens,
+    pkv_decode_workspace_bytes,
+    pkv_paged_attn_decode,
+    pkv_paged_attn_prefill,
+    pkv_store_kv,
+    strerror,
+    version,
+)

@@ -1,0 +1,179 @@
+"""Thin ctypes binding of libpkv.so (declared in include/pkv.h).
+
+The functions carry the C names and only marshal arguments: torch tensors
+become device pointers, the current torch stream becomes the hipStream_t,
+and a non-zero status becomes a ``PKVError``.  Every step of the
+computation runs in the HIP kernels of libpkv.so; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOSPACE, PKV_EHIP = 0, 1, 2, 3, 4
+
+# Exported symbols and their C signatures, in header order.
+_c_void_p, _i32, _i64, _f32, _size = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_float, ctypes.c_size_t)
+SIGNATURES = {
+    "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_store_kv": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                                    _c_void_p, _i64, _i32, _i32, _c_void_p]),
+    "pkv_decode_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_split_tokens": (_i32, [_i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_decode": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _i32, _c_void_p, _i32, _i32,
+        _i32, _i32, _i32, _f32, _i32, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "pkv_paged_attn_prefill": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _i32,
+        _i64, _c_void_p, _i32, _i32, _i32, _i32, _f32, _c_void_p, _c_void_p]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class PKVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpkv.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_attention_out_amd.build`"
+                " (there is no non-HIP fallback)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def strerror(status: int) -> str:
+    return lib().pkv_strerror(status).decode()
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+def _check(status: int, where: str):
+    if status != PKV_OK:
+        raise PKVError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def pkv_store_kv(k_new: torch.Tensor, v_new: torch.Tensor, out_loc: torch.Tensor,
+                 k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Scatter k_new/v_new ``[T, Hkv, d]`` into pool rows ``out_loc``."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, torch.bfloat16, n)
+    _dev(out_loc, torch.int32, "out_loc")
+    T = out_loc.numel()
+    Hkv, d = k_cache.shape[-2], k_cache.shape[-1]
+    slots = k_cache.numel() // (Hkv * d)
+    _check(lib().pkv_store_kv(_ptr(k_new), _ptr(v_new), _ptr(out_loc), T, _ptr(k_cache),
+                              _ptr(v_cache), slots, Hkv, d, _stream(k_cache)), "pkv_store_kv")
+
+
+def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                               head_dim: int, max_seq_len: int, split_tokens: int = 0) -> int:
+    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 max_seq_len, split_tokens))
+
+
+def pkv_decode_split_tokens(num_seqs: int, num_kv_heads: int, max_seq_len: int,
+                            split_tokens: int = 0) -> int:
+    return int(lib().pkv_decode_split_tokens(num_seqs, num_kv_heads, max_seq_len, split_tokens))
+
+
+def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                     split_tokens=0, device="cuda") -> Optional[torch.Tensor]:
+    """A zero-filled workspace of the size the decode call needs (or None)."""
+    nbytes = pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        max_seq_len, split_tokens)
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def pkv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                          softmax_scale: float, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          split_tokens: int = 0) -> torch.Tensor:
+    """Decode attention; q ``[B, Hq, d]`` -> out ``[B, Hq, d]`` (bf16)."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    _dev(page_table, torch.int32, "page_table")
+    _dev(seq_lens, torch.int32, "seq_lens")
+    B, Hq, d = q.shape
+    num_pages, ps, Hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out")
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, Hkv, d, max_seq_len, split_tokens, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), ps, num_pages, _ptr(page_table),
+        page_table.shape[1], _ptr(seq_lens), B, max_seq_len, Hq, Hkv, d, softmax_scale,
+        split_tokens, _ptr(out), _ptr(workspace), ws_bytes, _stream(q)), "pkv_paged_attn_decode")
+    return out
+
+
+def pkv_paged_attn_prefill(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                           prefix_lens: torch.Tensor, max_q_len: int, max_seq_len: int,
+                           k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           page_table: torch.Tensor, softmax_scale: float,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal prefill with prefix; q ``[T, Hq, d]`` -> out ``[T, Hq, d]``."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    _dev(page_table, torch.int32, "page_table")
+    _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q")
+    _dev(prefix_lens, torch.int32, "prefix_lens")
+    T, Hq, d = q.shape
+    num_pages, ps, Hkv, _ = k_cache.shape
+    B = prefix_lens.numel()
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out")
+    _check(lib().pkv_paged_attn_prefill(
+        _ptr(q), _ptr(cu_seqlens_q), _ptr(prefix_lens), B, T, max_q_len, max_seq_len,
+        _ptr(k_cache), _ptr(v_cache), ps, num_pages, _ptr(page_table), page_table.shape[1], Hq,
+        Hkv, d, softmax_scale, _ptr(out), _stream(q)), "pkv_paged_attn_prefill")
+    return out

@@ -1,0 +1,139 @@
+"""The C ABI on the host: the library loads, exports what include/pkv.h
+declares, and rejects bad arguments before anything is enqueued.
+
+Every call here fails host-side validation, so no kernel is ever launched
+(the fake device pointers below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_attention_out_amd as pkv
+from paged_kv_attention_out_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("pkv_store_kv", "pkv_paged_attn_decode", "pkv_paged_attn_prefill",
+              "pkv_decode_workspace_bytes", "pkv_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = pkv.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pkv_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    assert set(_lib.SIGNATURES) == set(_declared())
+
+
+def test_strerror_and_version():
+    assert pkv.strerror(0) == "success"
+    for s in range(1, 5):
+        assert pkv.strerror(s) and pkv.strerror(s) != "unknown status"
+    assert pkv.strerror(99) == "unknown status"
+    assert "gfx950" in pkv.version()
+
+
+def _store(**kw):
+    a = dict(k_new=FAKE, v_new=FAKE, out_loc=FAKE, T=4, kc=FAKE, vc=FAKE, slots=64, hkv=8,
+             d=64, stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_store_kv(a["k_new"], a["v_new"], a["out_loc"], a["T"], a["kc"],
+                                  a["vc"], a["slots"], a["hkv"], a["d"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_new=None), 1), (dict(out_loc=None), 1), (dict(kc=None), 1),
+    (dict(T=-1), 1), (dict(slots=0), 1), (dict(hkv=0), 1), (dict(d=12), 1),
+    (dict(k_new=FAKE + 8), 1), (dict(vc=FAKE + 2), 1),
+    (dict(T=0, k_new=None, v_new=None, out_loc=None), 0),
+])
+def test_store_kv_validation(kw, status):
+    assert _store(**kw) == status
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ps=16, pages=100, pt=FAKE, stride=128, seq=FAKE, B=4,
+             maxlen=2048, hq=32, hkv=8, d=64, scale=0.125, split=0, out=FAKE, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_paged_attn_decode(
+        a["q"], a["kc"], a["vc"], a["ps"], a["pages"], a["pt"], a["stride"], a["seq"], a["B"],
+        a["maxlen"], a["hq"], a["hkv"], a["d"], a["scale"], a["split"], a["out"], a["ws"],
+        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(pt=None), 1), (dict(seq=None), 1), (dict(out=None), 1),
+    (dict(B=-1), 1), (dict(hq=30), 1), (dict(hkv=0), 1), (dict(maxlen=0), 1),
+    (dict(scale=0.0), 1), (dict(scale=-1.0), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=float("nan")), 1), (dict(stride=127), 1), (dict(pages=0), 1),
+    (dict(split=8), 1), (dict(split=17), 1), (dict(split=70000), 1), (dict(q=FAKE + 4), 1),
+    (dict(ps=24), 2), (dict(ps=8), 2), (dict(ps=512), 2), (dict(d=96), 2), (dict(d=256), 2),
+    (dict(hq=64), 2),                       # 8 query heads per KV head
+    (dict(wsb=100, ws=FAKE), 3),            # needs a workspace, too small
+    (dict(B=0), 0),
+])
+def test_decode_validation(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_decode_workspace_sizes():
+    # one split per request: no workspace
+    assert pkv.pkv_decode_workspace_bytes(1, 4, 2, 64, 64) == 0
+    assert pkv.pkv_decode_split_tokens(1, 2, 64) == 64
+    n = pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 2048)
+    s = pkv.pkv_decode_split_tokens(64, 8, 2048)
+    nsm = -(-2048 // s)
+    assert nsm > 1
+    assert n >= 64 * 8 * 4 + 2 * 64 * 8 * nsm * 4 * 4 + 64 * 8 * nsm * 4 * 64 * 4
+    assert pkv.pkv_decode_split_tokens(64, 8, 2048, 48) == 48
+    assert pkv.pkv_decode_split_tokens(64, 8, 2048, 40) == 0   # not a multiple of 16
+    assert pkv.pkv_decode_workspace_bytes(64, 30, 8, 64, 2048) == 0  # invalid grouping
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, cu=FAKE, prefix=FAKE, B=4, T=100, maxq=50, maxlen=1000, kc=FAKE, vc=FAKE,
+             ps=16, pages=100, pt=FAKE, stride=64, hq=32, hkv=8, d=64, scale=0.125, out=FAKE,
+             stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_paged_attn_prefill(
+        a["q"], a["cu"], a["prefix"], a["B"], a["T"], a["maxq"], a["maxlen"], a["kc"], a["vc"],
+        a["ps"], a["pages"], a["pt"], a["stride"], a["hq"], a["hkv"], a["d"], a["scale"],
+        a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(prefix=None), 1), (dict(out=None), 1),
+    (dict(B=0), 1), (dict(B=-2), 1), (dict(T=-1), 1), (dict(maxq=0), 1), (dict(maxlen=0), 1),
+    (dict(hq=33), 1), (dict(scale=0.0), 1), (dict(stride=62), 1), (dict(pages=0), 1),
+    (dict(kc=FAKE + 8), 1),
+    (dict(ps=48), 2), (dict(d=80), 2), (dict(hq=128), 2), (dict(d=128, hq=64), 2),
+    (dict(T=0, q=None), 0),
+])
+def test_prefill_validation(kw, status):
+    assert _prefill(**kw) == status
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

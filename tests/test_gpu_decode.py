@@ -1,0 +1,171 @@
+"""Paged decode attention on the GPU against the float64 oracle.
+
+Small cases compare every output element; the full-size workloads compare
+every element where the oracle is quick (tiny, Llama-shaped) and sampled
+requests otherwise (Qwen-shaped, long context).  Invariants: physical page
+permutation (bit-exact), run-to-run determinism (bit-exact), independence
+of the split length (within tolerance), a single visible token returns its
+V row exactly, zero query gives the mean of V, empty requests give zeros,
+and the workspace counters return to zero."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_out_amd as pkv
+from oracle import paged_attention as orc
+from paged_kv_attention_out_amd import inputs
+
+from gpu_helpers import assert_close, compact, f64, host_pools, run_decode, run_store
+
+pytestmark = pytest.mark.gpu
+
+# (B, Hq, Hkv, d, ps, seq_lens, split_tokens) -- every (d, g) instantiation,
+# tails of every length class, several splits per request
+CASES = [
+    (3, 4, 4, 64, 16, [1, 17, 64], 0),
+    (5, 8, 4, 64, 16, [15, 16, 100, 333, 1000], 64),
+    (2, 8, 2, 64, 32, [2000, 77], 128),
+    (4, 16, 8, 128, 256, [1, 255, 256, 1500], 0),
+    (4, 16, 8, 128, 256, [700, 2000, 513, 20], 256),
+    (3, 8, 8, 128, 16, [40, 1, 300], 32),
+    (2, 8, 2, 128, 64, [911, 16], 16),
+    (3, 2, 1, 64, 128, [129, 4000, 3], 0),
+]
+
+
+def _ids(c):
+    return f"B{c[0]}-hq{c[1]}-hkv{c[2]}-d{c[3]}-ps{c[4]}-split{c[6]}"
+
+
+def _oracle(w, requests=None, heads=None):
+    kc, vc = host_pools(w)
+    return orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale,
+                      requests=requests, heads=heads)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_decode_small(case):
+    B, hq, hkv, d, ps, lens, split = case
+    print(f"decode case {_ids(case)} lens={lens}", flush=True)
+    w = inputs.build_decode(B, hq, hkv, d, ps, lens, seed=sum(lens) + d, device="cuda",
+                            store_new=True)
+    ref = _oracle(w)                    # host copies taken before any kernel runs
+    run_store(w)
+    out = run_decode(w, split_tokens=split)
+    torch.cuda.synchronize()
+    assert_close(f64(out), ref, _ids(case))
+
+
+def test_decode_tiny_workload():
+    w = inputs.make_workload("tiny_decode", device="cuda")
+    out = run_decode(w)
+    torch.cuda.synchronize()
+    assert_close(f64(out), _oracle(w), "tiny_decode")
+
+
+def test_decode_llama_workload():
+    w = inputs.make_workload("llama_decode")          # generated on the host, then copied
+    ref = _oracle(w)
+    w = w.to("cuda")
+    run_store(w)
+    out = run_decode(w)
+    torch.cuda.synchronize()
+    print("llama_decode max/mean err", assert_close(f64(out), ref, "llama_decode"))
+
+
+@pytest.mark.parametrize("name,nreq", [("qwen_decode", 12), ("long_decode", 2)])
+def test_decode_large_workload_sampled(name, nreq):
+    print(f"decode workload={name}", flush=True)
+    w = inputs.make_workload(name, device="cuda")
+    out = run_decode(w)
+    torch.cuda.synchronize()
+    order = np.argsort(w.seq_lens_np)
+    reqs = sorted(set([int(order[-1]), int(order[0])] +
+                      np.random.default_rng(0).choice(w.num_seqs, nreq, replace=False).tolist()))
+    reqs = reqs[:max(nreq, 2)]
+    kc, vc, table = compact(w, reqs)
+    q = inputs.bf16_bits(w.q)[reqs]
+    ref = orc.decode(q, kc, vc, table, w.seq_lens_np[reqs], w.scale)
+    print(f"{name} requests {reqs} max/mean err",
+          assert_close(f64(out)[reqs], ref, name))
+
+
+def test_decode_page_permutation_is_bit_exact():
+    w = inputs.build_decode(4, 8, 2, 64, 16, [300, 1, 77, 1024], seed=21, device="cuda")
+    a = run_decode(w, split_tokens=64).clone()
+    perm = torch.randperm(w.num_pages, generator=torch.Generator().manual_seed(5))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(len(perm))
+    k2 = torch.empty_like(w.k_cache)
+    v2 = torch.empty_like(w.v_cache)
+    k2[perm.cuda()] = w.k_cache
+    v2[perm.cuda()] = w.v_cache
+    w.k_cache, w.v_cache = k2, v2
+    w.page_table = perm.cuda().to(torch.int32)[w.page_table.long()]
+    b = run_decode(w, split_tokens=64)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_deterministic_and_split_invariant():
+    w = inputs.build_decode(3, 16, 8, 128, 16, [3000, 999, 2048], seed=22, device="cuda")
+    ref = _oracle(w)
+    outs = {}
+    for split in (16, 48, 256, 1024, 0):
+        a = run_decode(w, split_tokens=split).clone()
+        b = run_decode(w, split_tokens=split).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), split
+        assert_close(f64(a), ref, f"split {split}")
+        outs[split] = f64(a)
+    for s, o in outs.items():
+        assert np.abs(o - outs[0]).max() <= 2e-2, s
+
+
+def test_decode_single_token_returns_v_exactly():
+    w = inputs.build_decode(3, 8, 2, 64, 16, [1, 1, 1], seed=23, device="cuda")
+    out = run_decode(w)
+    torch.cuda.synchronize()
+    v = w.v_cache.view(-1, 2, 64)
+    for r in range(3):
+        slot = int(w.page_table_np[r, 0]) * 16
+        for h in range(8):
+            assert torch.equal(out[r, h].view(torch.int16), v[slot, h // 4].view(torch.int16))
+
+
+def test_decode_zero_query_is_mean_of_v():
+    w = inputs.build_decode(2, 4, 2, 128, 16, [37, 500], seed=24, device="cuda")
+    w.q.zero_()
+    out = run_decode(w, split_tokens=64)
+    torch.cuda.synchronize()
+    kc, vc = host_pools(w)
+    for r in range(2):
+        V = orc.bf16_to_f64(vc.reshape(-1, 2, 128)[orc.request_slots(
+            w.page_table_np[r], int(w.seq_lens_np[r]), 16)])
+        for h in range(4):
+            ref = V[:, h // 2].mean(axis=0)
+            assert np.abs(f64(out[r, h]) - ref).max() <= 2e-2
+
+
+def test_decode_empty_request_gives_zeros():
+    w = inputs.build_decode(3, 8, 2, 64, 16, [50, 1, 70], seed=25, device="cuda")
+    w.seq_lens[1] = 0
+    out = torch.full_like(w.q, 7.0)
+    run_decode(w, out=out, split_tokens=16)
+    torch.cuda.synchronize()
+    assert (out[1] == 0).all()
+    w.seq_lens_np = w.seq_lens_np.copy()
+    w.seq_lens_np[1] = 1
+    ref = _oracle(w, requests=[0, 2])
+    assert_close(f64(out), ref, "empty request")
+
+
+def test_decode_workspace_counters_return_to_zero():
+    w = inputs.build_decode(4, 8, 4, 64, 16, [900, 33, 1500, 16], seed=26, device="cuda")
+    ws = pkv.decode_workspace(4, 8, 4, 64, w.max_seq_len, 64, "cuda")
+    for _ in range(3):
+        run_decode(w, split_tokens=64, workspace=ws)
+    torch.cuda.synchronize()
+    assert (ws[: 4 * 4 * 4] == 0).all()
+    assert_close(f64(run_decode(w, split_tokens=64, workspace=ws)), _oracle(w), "reuse")
