@@ -118,8 +118,8 @@ int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *
  * over j = 0 .. seq_lens[r]-1, with K[r, j, kvh] the row of slot
  * page_table[r, j / page_size] * page_size + j % page_size.  Long contexts
- * are cut into splits of split_tokens tokens that run in parallel and are
- * merged in the same launch (flash-decoding).
+ * are cut into splits of split_tokens tokens that run in parallel; a second
+ * kernel on the same stream merges the splits (flash-decoding).
  *
  *   q            : [num_seqs, num_q_heads, head_dim] bf16
  *   k_cache,
@@ -135,11 +135,12 @@ int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *   softmax_scale: finite and > 0 (typically 1/sqrt(head_dim))
  *   split_tokens : 0 = automatic, else a multiple of 16 in [16, 65536]
  *   out          : [num_seqs, num_q_heads, head_dim] bf16 (round to nearest even)
- *   workspace    : device buffer of at least pkv_decode_workspace_bytes(...)
- *                  bytes, 256-byte aligned, ZERO-FILLED before its first use;
- *                  every call returns its counter words to zero, so one
- *                  buffer serves any sequence of calls ordered on a stream.
- *                  May be NULL when the required size is 0.
+ *   workspace    : device scratch of at least pkv_decode_workspace_bytes(...)
+ *                  bytes, 256-byte aligned, for the per-split partial results
+ *                  (running max, sum and un-normalised output in fp32); its
+ *                  contents on entry do not matter.  Calls sharing one
+ *                  workspace must be ordered (e.g. on one stream).  May be
+ *                  NULL when the required size is 0.
  */
 int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                           int32_t page_size, int64_t num_pages,

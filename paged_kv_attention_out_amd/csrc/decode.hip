@@ -3,35 +3,48 @@
 // prepare_decode: context_lens + block_tables; mini-sglang "Engine Class",
 // Key Attributes: page_table).
 //
-// Work unit = one wavefront per (request r, KV head kvh, split s).  A split
-// is `split` consecutive tokens; a request with n tokens has ceil(n/split)
-// splits.  The wave walks its tokens 16 at a time ("groups"):
+// Two kernels on the caller's stream:
 //
-//   * K rows: lane l holds token (l % 16) of the group and the 16-byte
-//     pieces [c*D/4, (c+1)*D/4) of its row, c = l / 16.  Those are exactly
-//     the B operands of D/32 MFMA 16x16x32 bf16 instructions that compute
-//     S = Q K^T for the group; each piece is a 16-byte global load and one
-//     group of one page reads whole 128/256-byte rows.
-//   * Q: the A operand has 16 rows; row m holds query head kvh*g + m % g,
-//     so the g heads are replicated and every lane receives the scores of
-//     all g heads for its own token (g = 1, 2, 4).
-//   * Softmax: each lane keeps its own running max / sum per head (base-2,
-//     scale * log2(e) folded in) and rescales lazily: only when some lane's
-//     score exceeds its max by more than kTau, so p <= 2^kTau.  The result
-//     is the same function; only the reference point of the exponentials
+// decode_split_kernel -- one wavefront per (request r, KV head kvh, split s).
+//   A split is `split` consecutive tokens; a request with n tokens has
+//   ceil(n/split) splits.  The wave walks its tokens 16 at a time ("groups"):
+//   * Lane l holds token j = l % 16 of the group and, for each 32-dim block
+//     kk, the 8 dims 32*kk + 8*c .. +7 with c = l / 16.  Those are the B
+//     operands of D/32 MFMA 16x16x32 bf16 instructions computing S = Q K^T
+//     (the contraction order over head dims is a free permutation; Q uses the
+//     same one), and every load instruction reads 64 contiguous bytes of each
+//     of the 16 rows.
+//   * Q: the A operand has 16 rows; row m holds query head kvh*g + m % g, so
+//     the g heads are replicated and every lane receives the scores of all g
+//     heads for its own token (g = 1, 2, 4).
+//   * K/V rows of NBUF groups are loaded together (one register buffer per
+//     group) and then computed in order.
+//   * Softmax: each lane keeps its own running max / sum per head, base 2
+//     with scale * log2(e) folded in, and rescales lazily: only when some
+//     lane's score exceeds its max by more than kTau, so p <= 2^kTau.  The
+//     function is unchanged; only the reference point of the exponentials
 //     moves.
-//   * PV: the V rows come in the same layout as K; each lane accumulates
-//     p * v for its token into o[g][D/4] in fp32 (VALU FMAs).
-//   * End of split: lanes holding the same dims are merged (max, rescale,
-//     sum); a request with one split writes bf16 output directly, otherwise
-//     the split writes (m, l, o) to the workspace and the last wave of the
-//     (r, kvh) to finish -- found with one device-scope atomic counter --
-//     merges the splits (flash-decoding) and resets the counter to zero.
+//   * PV: V rows arrive in the same layout; each lane accumulates p * v for
+//     its token into o[g][D/4] in fp32 (VALU FMAs).
+//   * End of split: the 16 token lanes holding the same dims are merged
+//     with DPP butterflies.  A request with one split writes bf16 output
+//     directly; otherwise the split writes (m, l, un-normalised o) to the
+//     workspace.
+// decode_combine_kernel -- one wavefront per (r, query head) with >= 2
+//   splits merges the partials (flash-decoding): M = max m_s,
+//   L = sum l_s 2^(m_s-M), out = sum o_s 2^(m_s-M) / L.
 //
 // Bandwidth: every K/V byte of the context is read once; partials add
-// splits * g * (D + 2) * 4 bytes per (r, kvh).
+// splits * g * (D + 2) * 4 bytes written and read per (r, kvh).
 
 #include "pkv_common.h"
+
+#ifndef PKV_DECODE_NBUF_D64
+#define PKV_DECODE_NBUF_D64 4
+#endif
+#ifndef PKV_DECODE_NBUF_D128
+#define PKV_DECODE_NBUF_D128 4
+#endif
 
 namespace {
 
@@ -44,10 +57,9 @@ struct DecodeParams {
   const int32_t* page_table;
   const int32_t* seq_lens;
   uint16_t* out;
-  int32_t* counters;  // [B * Hkv], zero between calls
-  float* ws_m;        // [B * Hkv * n_split_max * g]
+  float* ws_m;  // [B * Hkv * n_split_max * g]
   float* ws_l;
-  float* ws_o;        // [B * Hkv * n_split_max * g * D]
+  float* ws_o;  // [B * Hkv * n_split_max * g * D]
   int64_t num_pages;
   int32_t page_size;
   int32_t page_shift;
@@ -63,40 +75,125 @@ struct DecodeParams {
 
 constexpr float kTau = 8.0f;
 
-__device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
+// DPP lane exchanges inside a row of 16 lanes.  After the two quad steps
+// every lane of a quad holds the quad's total; row_half_mirror pairs quad 0
+// with quad 1 (and 2 with 3), row_mirror pairs the two halves of the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kHalfMirror>(v));
+  v = fmaxf(v, dpp<kRowMirror>(v));
   return v;
 }
 
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kHalfMirror>(v);
+  v += dpp<kRowMirror>(v);
   return v;
 }
+
+#ifdef PKV_DECODE_WAVES_PER_EU
+#define PKV_DECODE_OCC __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU)))
+#else
+#define PKV_DECODE_OCC
+#endif
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
-  constexpr int KCH = D / 32;  // 16-byte pieces per lane per row == MFMAs per group
-  constexpr int DL = D / 4;    // dims per lane
+struct DecodeTraits {
+  // groups of 16 tokens per load chunk (even: PV consumes groups in pairs)
+  static constexpr int NBUF = D == 64 ? PKV_DECODE_NBUF_D64 : PKV_DECODE_NBUF_D128;
+  static_assert(NBUF % 2 == 0, "chunks hold pairs of groups");
+};
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
-  const int split = (int)(unit % p.n_split_max);
-  const int64_t rk = unit / p.n_split_max;
-  if (rk >= (int64_t)p.num_seqs * p.num_kv_heads) return;
-  const int kvh = (int)(rk % p.num_kv_heads);
-  const int r = (int)(rk / p.num_kv_heads);
-  const int j = lane & 15;  // token within the group
-  const int c = lane >> 4;  // dim quarter
+// Per-split kernel, one wavefront per (request, KV head, split).
+//
+// Per group of 16 tokens (lane l: token l%16 of the group, c = l/16):
+//   S^T = K Q^T on MFMA 16x16x32: A = the K rows as loaded (lane l holds 8
+//   dims 32kk+8c.. of token l%16), B = Q^T (column n = query head n % G,
+//   so the G heads are replicated over the 16 columns).  Lane l receives
+//   the scores of tokens 4c..4c+3 for query head (l%16) % G.
+// Per pair of groups (32 tokens), O += P V on MFMA 16x16x32:
+//   A = P: row = query head column, key slot (c, i) = token 4c+i of the
+//   first group (i < 4) or of the second (i >= 4) -- exactly the S^T
+//   registers this lane already holds, rounded to bf16.
+//   B = V with the same key order: the V rows are staged row-major in LDS
+//   and read back key-contiguous with ds_read_b64_tr_b16, which, within
+//   each 16-lane group, hands lane 4q+e element e of the 8-byte chunks that
+//   lanes q, q+4, q+8, q+12 point at; pointing lane L at row k0 + L/4,
+//   column 4*(L%4) gives every lane 4 consecutive keys of one dim.
+//   O (16 head rows x D dims) lives in D/16 accumulators of 4 registers;
+//   row 4c+i is query head i % G.
+template <int D, int G>
+__global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
+  constexpr int KCH = D / 32;  // 16-byte pieces per lane per row == QK MFMAs per group
+  constexpr int NT = D / 16;   // 16-dim tiles of the output == PV MFMAs per pair
+  constexpr int NBUF = DecodeTraits<D, G>::NBUF;
+  constexpr int VPITCH = D + 8;  // LDS row pitch (bf16): conflict-free rows
+  static_assert(G == 1 || G == 2 || G == 4, "query heads per KV head");
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[NBUF * 16 * VPITCH];
+
+  const int lane = threadIdx.x;
+  // unit = (split * B + r) * Hkv + kvh.  The KV heads of one (request,
+  // split) are dispatched together and sweep the same pages, so between
+  // them they read whole rows of each page; split-major order puts the
+  // splits that may be empty (past a short request's end) last.
+  const uint32_t unit = blockIdx.x;  // one wave per block
+  const uint32_t sr = unit / (uint32_t)p.num_kv_heads;
+#ifdef PKV_DECODE_NO_ROTATE
+  const int kvh = (int)(unit % (uint32_t)p.num_kv_heads);
+#else
+  // Rotate the heads over the dispatch slots from one (request, split) to
+  // the next: blocks land on XCDs round-robin, so every XCD sees every
+  // head's offset within the page rows instead of always the same one.
+  const int kvh = (int)((unit + sr) % (uint32_t)p.num_kv_heads);
+#endif
+  const int r = (int)(sr % (uint32_t)p.num_seqs);
+  const int split = (int)(sr / (uint32_t)p.num_seqs);
+  if (split >= p.n_split_max) return;
+  const int64_t rk = (int64_t)r * p.num_kv_heads + kvh;
+  const int j = lane & 15;  // token within the group / score column
+  const int c = lane >> 4;  // 16-byte piece within each 64-byte block / token quad
+  const int hcol = j % G;   // query head of this lane's score column
+  const int t_begin = split * p.split;
+
+  // Issue every load that does not depend on the length first: the length
+  // itself, the Q fragments and the split's first page-table window.
+  int n = uniform(p.seq_lens[r]);
+
+  // Q^T fragments (B operand): column j holds head kvh*G + j % G.
+  bf16x8 qb[KCH];
+  {
+    const uint16_t* qp = p.q + ((int64_t)r * p.num_q_heads + (int64_t)kvh * G + hcol) * D + 8 * c;
+#pragma unroll
+    for (int kk = 0; kk < KCH; ++kk) qb[kk] = as_bf16x8(ld16(qp + 32 * kk));
+  }
+
+  // Page ids, one window of up to 64 logical pages at a time (lane i holds
+  // page base + i), so the streaming loop below issues no loads other than
+  // K/V rows and needs no branches to find a page.  Entries past the
+  // request's last page may be read but are never used.
+  const int32_t* pt = p.page_table + (int64_t)r * p.pt_stride;
+  int ptv = 0, lp_base = 0;
+  auto load_window = [&](int base) {
+    lp_base = base;
+    const int i0 = base + lane;
+    const int v = i0 < p.pt_stride ? pt[i0] : 0;
+    ptv = (v < 0 || (int64_t)v >= p.num_pages) ? 0 : v;  // keep accesses in the pool
+  };
+  load_window(t_begin >> p.page_shift);
 
   uint16_t* out_rk = p.out + ((int64_t)r * p.num_q_heads + (int64_t)kvh * G) * D;
-  int n = uniform(p.seq_lens[r]);
   n = n > p.max_seq_len ? p.max_seq_len : n;
   if (n <= 0) {
     if (split == 0)
@@ -106,213 +203,297 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
   const int ns = (n + p.split - 1) / p.split;
   if (split >= ns) return;
-  const int t_begin = split * p.split;
   const int t_end = min(n, t_begin + p.split);
-
-  // Q fragments (A operand): row j holds head kvh*G + j % G.
-  bf16x8 qa[KCH];
-  {
-    const uint16_t* qp =
-        p.q + ((int64_t)r * p.num_q_heads + (int64_t)kvh * G + (j % G)) * D + c * DL;
-#pragma unroll
-    for (int kk = 0; kk < KCH; ++kk) qa[kk] = as_bf16x8(ld16(qp + 8 * kk));
-  }
-
-  // Page ids of the split, 64 logical pages per window (lane i holds one).
-  const int32_t* pt = p.page_table + (int64_t)r * p.pt_stride;
-  const int lp_last = (t_end - 1) >> p.page_shift;
-  int lp_base = t_begin >> p.page_shift;
-  auto load_window = [&](int base) {
-    const int idx = base + lane;
-    int v = idx <= lp_last ? pt[idx] : 0;
-    return (v < 0 || (int64_t)v >= p.num_pages) ? 0 : v;  // keep accesses in the pool
-  };
-  int ptv = load_window(lp_base);
 
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
   const int64_t page_elems = row_elems << p.page_shift;
-  const int lane_off = (j * p.num_kv_heads + kvh) * D + c * DL;
+  const int lane_off = (j * p.num_kv_heads + kvh) * D + 8 * c;
 
   auto group_offset = [&](int t0) -> int64_t {
-    const int lp = t0 >> p.page_shift;
-    if (lp - lp_base >= 64) {
-      lp_base = lp;
-      ptv = load_window(lp_base);
-    }
-    const int page = __builtin_amdgcn_readlane(ptv, lp - lp_base);
+    const int i = uniform((t0 >> p.page_shift) - lp_base);  // < 64 inside a window
+    const int page = __builtin_amdgcn_readlane(ptv, i);
     return (int64_t)page * page_elems + (int64_t)(t0 & (p.page_size - 1)) * row_elems;
   };
-  auto load_kv = [&](int64_t goff, int loff, uint4 (&kb)[KCH], uint4 (&vb)[KCH]) {
-    const uint16_t* kp = p.k_cache + goff + loff;
-    const uint16_t* vp = p.v_cache + goff + loff;
+
+  uint4 kb[NBUF][KCH], vb[NBUF][KCH];
+  auto load_group = [&](int t0, int loff, int buf) {
+    const int64_t goff = group_offset(t0) + loff;
+    const uint16_t* kp = p.k_cache + goff;
+    const uint16_t* vp = p.v_cache + goff;
 #pragma unroll
-    for (int kk = 0; kk < KCH; ++kk) kb[kk] = ld16(kp + 8 * kk);
+    for (int b = 0; b < NBUF; ++b) {
+      if (b == buf) {
 #pragma unroll
-    for (int kk = 0; kk < KCH; ++kk) vb[kk] = ld16(vp + 8 * kk);
+        for (int kk = 0; kk < KCH; ++kk) kb[b][kk] = ld16(kp + 32 * kk);
+#pragma unroll
+        for (int kk = 0; kk < KCH; ++kk) vb[b][kk] = ld16(vp + 32 * kk);
+      }
+    }
   };
-
-  float o[G][DL];
-  float m[G], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < DL; ++i) o[h][i] = 0.f;
-  }
-
-  auto process = [&](const uint4 (&kb)[KCH], const uint4 (&vb)[KCH], int valid) {
+  // K rows of a group -> S^T scores (4 tokens per lane)
+  auto scores = [&](int buf) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+    for (int b = 0; b < NBUF; ++b)
+      if (b == buf) {
+#pragma unroll
+        for (int kk = 0; kk < KCH; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[b][kk]), qb[kk], acc, 0, 0,
+                                                        0);
+      }
+    return acc;
+  };
+  // V rows of a group -> LDS slot (16 rows), row-major
+  auto stage_v = [&](int buf, int slot) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b)
+      if (b == buf) {
+#pragma unroll
+        for (int kk = 0; kk < KCH; ++kk)
+          *reinterpret_cast<uint4*>(&vlds[(slot * 16 + j) * VPITCH + 32 * kk + 8 * c]) = vb[b][kk];
+      }
+  };
+  auto zero_v = [&](int slot) {
+#pragma unroll
     for (int kk = 0; kk < KCH; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(kb[kk]), acc, 0, 0, 0);
-    float x[G];
-    bool grow = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      x[h] = acc[h] * p.scale_log2;
-      if (valid < 16) x[h] = j < valid ? x[h] : kNegInf;
-      grow |= x[h] > m[h] + kTau;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], x[h]);
-        const float a = mn == kNegInf ? 0.f : fast_exp2(m[h] - mn);
-        l[h] *= a;
-#pragma unroll
-        for (int i = 0; i < DL; ++i) o[h][i] *= a;
-        m[h] = mn;
-      }
-    }
-    float pr[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      pr[h] = fast_exp2(x[h] - m[h]);
-      if (valid < 16) pr[h] = j < valid ? pr[h] : 0.f;
-      l[h] += pr[h];
-    }
-    float v[DL];
-#pragma unroll
-    for (int kk = 0; kk < KCH; ++kk) {
-      const uint32_t w[4] = {vb[kk].x, vb[kk].y, vb[kk].z, vb[kk].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * kk + 2 * e] = bf16_lo(w[e]);
-        v[8 * kk + 2 * e + 1] = bf16_hi(w[e]);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < DL; ++i) o[h][i] = fmaf(pr[h], v[i], o[h][i]);
+      *reinterpret_cast<uint4*>(&vlds[(slot * 16 + j) * VPITCH + 32 * kk + 8 * c]) =
+          make_uint4(0, 0, 0, 0);
   };
 
-  // Main loop: double-buffered register prefetch of whole groups.
-  const int len = t_end - t_begin;
-  const int tail = len & 15;
-  const int nfull = len >> 4;
-  uint4 kA[KCH], vA[KCH], kB[KCH], vB[KCH];
-  int g = 0;
-  if (nfull > 0) load_kv(group_offset(t_begin), lane_off, kA, vA);
-  for (; g + 1 < nfull; g += 2) {
-    load_kv(group_offset(t_begin + 16 * (g + 1)), lane_off, kB, vB);
-    process(kA, vA, 16);
-    if (g + 2 < nfull) load_kv(group_offset(t_begin + 16 * (g + 2)), lane_off, kA, vA);
-    process(kB, vB, 16);
-  }
-  if (g < nfull) process(kA, vA, 16);
-  if (tail) {
-    // rows past the end are replaced by the last valid row (finite data),
-    // and their probabilities are forced to zero
-    const int jr = j < tail ? j : tail - 1;
-    load_kv(group_offset(t_begin + 16 * nfull), (jr * p.num_kv_heads + kvh) * D + c * DL, kA,
-            vA);
-    process(kA, vA, tail);
-  }
-
-  // Merge the 16 token lanes that hold the same dims.
+  f32x4 o[NT];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float M = max16(m[h]);
-    const float a = m[h] == kNegInf ? 0.f : fast_exp2(m[h] - M);
-    m[h] = M;
-    l[h] = sum16(l[h] * a);
+  for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_all[G];  // running max per query head, the same in every lane
 #pragma unroll
-    for (int i = 0; i < DL; ++i) o[h][i] = sum16(o[h][i] * a);
-  }
+  for (int h = 0; h < G; ++h) m_all[h] = kNegInf;
+  float m_own = kNegInf;  // m_all[hcol]
+  float l_own = 0.f;      // this lane's share of the row sum of head hcol
 
-  if (ns == 1) {
-    if (j == 0) {
+  const int trq = j & 3, trj = j >> 2;  // transpose-read lane roles
+
+  // One pair of groups: softmax of the 32 scores, then O += P V.
+  // va / vbv: valid tokens of each group (0 = absent group).
+  auto pv_pair = [&](f32x4 sa, f32x4 sb, int va, int vbv, int slot_a, int slot_b) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = sa[i] * p.scale_log2;
+      x[4 + i] = sb[i] * p.scale_log2;
+    }
+    if (va < 16 || vbv < 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = 4 * c + i < va ? x[i] : kNegInf;
+        x[4 + i] = 4 * c + i < vbv ? x[4 + i] : kNegInf;
+      }
+    }
+    float lm = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
+    if (__any(lm > m_own + kTau)) {
+      // new running max of every head: max over the lanes holding it
+      float alpha[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float inv = 1.f / l[h];
-        uint4* dst = reinterpret_cast<uint4*>(out_rk + h * D + c * DL);
+        float v = hcol == h ? lm : kNegInf;
 #pragma unroll
-        for (int q4 = 0; q4 < DL / 8; ++q4) {
-          uint4 w;
-          w.x = pack_bf16x2(o[h][8 * q4 + 0] * inv, o[h][8 * q4 + 1] * inv);
-          w.y = pack_bf16x2(o[h][8 * q4 + 2] * inv, o[h][8 * q4 + 3] * inv);
-          w.z = pack_bf16x2(o[h][8 * q4 + 4] * inv, o[h][8 * q4 + 5] * inv);
-          w.w = pack_bf16x2(o[h][8 * q4 + 6] * inv, o[h][8 * q4 + 7] * inv);
-          dst[q4] = w;
-        }
+        for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+        const float mn = fmaxf(m_all[h], v);
+        alpha[h] = mn == kNegInf ? 0.f : fast_exp2(m_all[h] - mn);
+        m_all[h] = mn;
       }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i] *= alpha[i % G];
+      float a_own = alpha[0];
+      m_own = m_all[0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) {
+        a_own = hcol == h ? alpha[h] : a_own;
+        m_own = hcol == h ? m_all[h] : m_own;
+      }
+      l_own *= a_own;
+    }
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      e[i] = fast_exp2(x[i] - m_own);
+      l_own += e[i];
+    }
+    uint4 pw;
+    pw.x = pack_bf16x2(e[0], e[1]);
+    pw.y = pack_bf16x2(e[2], e[3]);
+    pw.z = pack_bf16x2(e[4], e[5]);
+    pw.w = pack_bf16x2(e[6], e[7]);
+    const bf16x8 pa = as_bf16x8(pw);
+    const int ra = (slot_a * 16 + 4 * c + trj) * VPITCH + 4 * trq;
+    const int rb = (slot_b * 16 + 4 * c + trj) * VPITCH + 4 * trq;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const s16x4 lo = lds_read_tr16(vlds + ra + 16 * t);
+      const s16x4 hi = lds_read_tr16(vlds + rb + 16 * t);
+      const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vv), o[t], 0,
+                                                     0, 0);
+    }
+  };
+
+  // Main loop over windows of up to 64 pages.  Inside a window the groups
+  // go in chunks of NBUF: every K/V load of a chunk is issued first, then
+  // the pairs of groups are computed in order, each waiting only for its
+  // own rows.  No load is pending across a loop back-edge, so the wait
+  // counts the compiler derives are exact.
+  const int win_tokens = 64 << p.page_shift;
+  for (int w0 = t_begin; w0 < t_end; w0 += win_tokens) {
+    if (w0 != t_begin) load_window(w0 >> p.page_shift);
+    const int w_end = min(t_end, w0 + win_tokens);
+    const int len = w_end - w0;
+    const int tail = len & 15;
+    const int nfull = len >> 4;
+    int g = 0;
+    for (; g + NBUF <= nfull; g += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) load_group(w0 + 16 * (g + b), lane_off, b);
+      __builtin_amdgcn_sched_barrier(0);  // every load of the chunk issues first
+#pragma unroll
+      for (int b = 0; b < NBUF; b += 2) {
+        const f32x4 sa = scores(b), sb = scores(b + 1);
+        stage_v(b, b);
+        stage_v(b + 1, b + 1);
+        pv_pair(sa, sb, 16, 16, b, b + 1);
+      }
+    }
+    // Remaining full groups and the tail, two groups at a time; an absent
+    // second group contributes zero probabilities against zero rows.
+    const int ng = nfull + (tail ? 1 : 0);
+    for (; g < ng; g += 2) {
+      const int va = g < nfull ? 16 : tail;
+      const int vbv = g + 1 < nfull ? 16 : (g + 1 == nfull ? tail : 0);
+      const int ja = j < va ? j : va - 1;  // rows past the end repeat the last valid row
+      load_group(w0 + 16 * g, (ja * p.num_kv_heads + kvh) * D + 8 * c, 0);
+      f32x4 sb = {0.f, 0.f, 0.f, 0.f};
+      if (vbv > 0) {
+        const int jb = j < vbv ? j : vbv - 1;
+        load_group(w0 + 16 * (g + 1), (jb * p.num_kv_heads + kvh) * D + 8 * c, 1);
+        sb = scores(1);
+        stage_v(1, 1);
+      } else {
+        zero_v(1);
+      }
+      const f32x4 sa = scores(0);
+      stage_v(0, 0);
+      pv_pair(sa, sb, va, vbv, 0, 1);
+    }
+  }
+
+  // Row sums: a column's keys are spread over the four token quads.
+  float l_tot = l_own + __shfl_xor(l_own, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  float L[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) L[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_tot), h));
+  if (lane >= 16) return;  // lanes 0..15 hold head rows 0..3, dims 16t + lane
+
+  if (ns == 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float inv = 1.f / L[h];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) out_rk[h * D + 16 * t + lane] = to_bf16(o[t][h] * inv);
     }
     return;
   }
 
   // Partial (m, l, un-normalised o) of this split.
   const int64_t base = (rk * p.n_split_max + split) * G;
-  if (j == 0) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float* dst = p.ws_o + (base + h) * D + lane;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dst[16 * t] = o[t][h];
+  }
+  if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float4* dst = reinterpret_cast<float4*>(p.ws_o + (base + h) * D + c * DL);
-#pragma unroll
-      for (int q4 = 0; q4 < DL / 4; ++q4)
-        dst[q4] = make_float4(o[h][4 * q4], o[h][4 * q4 + 1], o[h][4 * q4 + 2], o[h][4 * q4 + 3]);
-    }
-    if (c == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        p.ws_m[base + h] = m[h];
-        p.ws_l[base + h] = l[h];
-      }
+      p.ws_m[base + h] = m_all[h];
+      p.ws_l[base + h] = L[h];
     }
   }
-  __threadfence();  // release the partial before counting this split as done
-  int prev = 0;
-  if (lane == 0) prev = atomicAdd(p.counters + rk, 1);
-  prev = __shfl(prev, 0);
-  if (prev != ns - 1) return;
-  __threadfence();  // acquire every other split's partial
+}
 
-  // Last split of (r, kvh): merge all partials into the bf16 output.
-  const int64_t rbase = rk * p.n_split_max * G;
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
+  constexpr int DPL = D / 64;  // output dims per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (request, query head)
+  if (rh >= (int64_t)p.num_seqs * p.num_q_heads) return;
+  const int r = (int)(rh / p.num_q_heads);
+  const int qh = (int)(rh % p.num_q_heads);
+  const int kvh = qh / G, h = qh % G;
+  int n = uniform(p.seq_lens[r]);
+  n = n > p.max_seq_len ? p.max_seq_len : n;
+  if (n <= 0) return;
+  const int ns = (n + p.split - 1) / p.split;
+  if (ns == 1) return;  // written by the split kernel
+  const int64_t sbase = ((int64_t)r * p.num_kv_heads + kvh) * p.n_split_max;  // split 0
+
+  // Global max over the splits (lane s reads split s, 64 at a time).
+  float M = kNegInf;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    float mv = s < ns ? p.ws_m[(sbase + s) * G + h] : kNegInf;
 #pragma unroll
-  for (int it = 0; it < (G * D + 63) / 64; ++it) {
-    const int idx = lane + 64 * it;
-    if (idx < G * D) {
-      const int h = idx / D;
-      const int d = idx - h * D;
-      float M = kNegInf;
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, p.ws_m[rbase + s * G + h]);
-      float L = 0.f, O = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const float w = fast_exp2(p.ws_m[rbase + s * G + h] - M);
-        L = fmaf(p.ws_l[rbase + s * G + h], w, L);
-        O = fmaf(p.ws_o[(rbase + s * G + h) * D + d], w, O);
+    for (int off = 32; off >= 1; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off));
+    M = fmaxf(M, mv);
+  }
+  float L = 0.f, acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    const float w = s < ns ? fast_exp2(p.ws_m[(sbase + s) * G + h] - M) : 0.f;
+    float t = s < ns ? p.ws_l[(sbase + s) * G + h] * w : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+    L += t;
+    // lane = output dim; eight splits' loads in flight per step
+    const int cnt = min(64, ns - s0);
+    int k = 0;
+    for (; k + 8 <= cnt; k += 8) {
+      float v[8][DPL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < DPL; ++i)
+          v[u][i] = p.ws_o[((sbase + s0 + k + u) * G + h) * D + lane + 64 * i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k + u));
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(v[u][i], wk, acc[i]);
       }
-      out_rk[h * D + d] = to_bf16(O / L);
+    }
+    for (; k < cnt; ++k) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+#pragma unroll
+      for (int i = 0; i < DPL; ++i)
+        acc[i] = fmaf(p.ws_o[((sbase + s0 + k) * G + h) * D + lane + 64 * i], wk, acc[i]);
     }
   }
-  if (lane == 0) p.counters[rk] = 0;
+  uint16_t* out = p.out + rh * D;
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) out[lane + 64 * i] = to_bf16(acc[i] * inv);
 }
 
 // ---- host side -------------------------------------------------------------
 
-constexpr int64_t kTargetUnits = 8192;
-constexpr int kMinAutoSplit = 256;
+// Automatic split: halve from one split per request until there are at
+// least kTargetUnits (request, KV head, split) units or splits reach
+// kMinAutoSplit tokens -- enough waves to keep HBM busy through the tail.
+constexpr int64_t kTargetUnits = 16384;
+constexpr int kMinAutoSplit = 128;
 
 int32_t choose_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                      int32_t split_tokens) {
@@ -327,13 +508,12 @@ int32_t choose_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct WsLayout {
-  size_t counters, m, l, o, total;
+  size_t m, l, o, total;
 };
 
 WsLayout ws_layout(int64_t rk, int64_t nsm, int g, int d) {
   WsLayout w;
-  w.counters = 0;
-  w.m = align256(rk * sizeof(int32_t));
+  w.m = 0;
   w.l = w.m + align256(rk * nsm * g * sizeof(float));
   w.o = w.l + align256(rk * nsm * g * sizeof(float));
   w.total = w.o + align256(rk * nsm * g * d * sizeof(float));
@@ -352,7 +532,12 @@ bool decode_shape_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
 
 template <int D, int G>
 int launch_decode(const DecodeParams& p, int64_t blocks, hipStream_t s) {
-  return pkv_host::launch(decode_kernel<D, G>, dim3((unsigned)blocks), dim3(256), s, p);
+  const int st = pkv_host::launch(decode_split_kernel<D, G>, dim3((unsigned)blocks), dim3(64),
+                                  s, p);
+  if (st != PKV_OK || p.n_split_max <= 1) return st;
+  const int64_t cblocks = ((int64_t)p.num_seqs * p.num_q_heads + 3) / 4;
+  return pkv_host::launch(decode_combine_kernel<D, G>, dim3((unsigned)cblocks), dim3(256), s,
+                          p);
 }
 
 }  // namespace
@@ -411,13 +596,16 @@ extern "C" int pkv_paged_attn_decode(const void* q, const void* k_cache, const v
     if (workspace_bytes < w.total) return PKV_ENOSPACE;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PKV_EINVAL;
     char* ws = static_cast<char*>(workspace);
-    p.counters = reinterpret_cast<int32_t*>(ws + w.counters);
     p.ws_m = reinterpret_cast<float*>(ws + w.m);
     p.ws_l = reinterpret_cast<float*>(ws + w.l);
     p.ws_o = reinterpret_cast<float*>(ws + w.o);
   }
   const int64_t units = rk * nsm;
-  const int64_t blocks = (units + 3) / 4;
+  // One wave per block: blocks go round-robin to the 8 XCDs, so with the KV
+  // head as the fastest unit index each XCD takes the same heads of every
+  // (request, split) -- equal work per XCD whatever the lengths -- while the
+  // heads sharing a page are dispatched together.
+  const int64_t blocks = units;
   if (blocks > INT32_MAX) return PKV_EINVAL;
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = static_cast<const uint16_t*>(k_cache);

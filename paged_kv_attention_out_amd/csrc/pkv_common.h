@@ -39,6 +39,15 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane 4q+e receives element e (16-bit) of the 8-byte chunks that
+// lanes q, q+4, q+8 and q+12 address.  `p` must point into LDS.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Wave-uniform broadcast of lane 0's value.

@@ -103,7 +103,7 @@ def test_decode_workspace_sizes():
     s = pkv.pkv_decode_split_tokens(64, 8, 2048)
     nsm = -(-2048 // s)
     assert nsm > 1
-    assert n >= 64 * 8 * 4 + 2 * 64 * 8 * nsm * 4 * 4 + 64 * 8 * nsm * 4 * 64 * 4
+    assert n >= 2 * 64 * 8 * nsm * 4 * 4 + 64 * 8 * nsm * 4 * 64 * 4  # (m, l) + o per split
     assert pkv.pkv_decode_split_tokens(64, 8, 2048, 48) == 48
     assert pkv.pkv_decode_split_tokens(64, 8, 2048, 40) == 0   # not a multiple of 16
     assert pkv.pkv_decode_workspace_bytes(64, 30, 8, 64, 2048) == 0  # invalid grouping

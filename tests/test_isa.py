@@ -4,7 +4,8 @@
   scalar atomics, scalar cache write-back / discard): every store and
   atomic the kernels make is a vector memory instruction.
 * No packed fp32 VALU instruction: the build disables them.
-* Every kernel uses MFMA where the design says it does.
+* Every kernel uses MFMA (and the LDS transpose read) where the design
+  says it does.
 
 This file names the forbidden mnemonics, so it is CPU-only and is kept out
 of GPU uploads.
@@ -42,4 +43,5 @@ def test_kernels_use_mfma(disasm):
     txt = {k.split("/")[-1].split(".")[0]: v for k, v in disasm.items()}
     assert "v_mfma_f32_16x16x32_bf16" in txt["decode"]
     assert "v_mfma_f32_32x32x16_bf16" in txt["prefill"]
-    assert "global_atomic_add" in txt["decode"]
+    assert "ds_read_b64_tr_b16" in txt["decode"]      # V read key-contiguous from LDS
+    assert "global_atomic" not in txt["decode"]       # splits merge in a second kernel
