@@ -71,6 +71,30 @@ def prefill_bytes(w) -> int:
     return kv + qo
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode call measured with rocprofv3 counters
+    (profiles/traffic.txt), or None when the kernel source has changed since
+    the counters were taken."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        wl, src, sha, fetch, write = line.split()
+        if wl != workload:
+            continue
+        try:
+            cur = hashlib.sha256(open(os.path.join(root, src), "rb").read()).hexdigest()
+        except OSError:
+            return None
+        return int(fetch) + int(write) if cur.startswith(sha) else None
+    return None
+
+
 # ---- GPU timing ----------------------------------------------------------------
 
 def _replicate(w, R):
@@ -268,7 +292,8 @@ def main():
                    "step": "store_kv + paged decode", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "decode_kernel",
+                     "traffic": measured_traffic(args.workload),
+                     "kernel": "decode call (decode_split_kernel + decode_combine_kernel)",
                      "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 2),
                      "kernel_us_median": round(r["kernel_ms_median"] * 1e3, 2),
                      "bytes_per_launch": decode_bytes(w)},
