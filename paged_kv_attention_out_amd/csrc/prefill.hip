@@ -55,19 +55,27 @@ struct PrefillParams {
 constexpr float kTau = 8.0f;
 constexpr int kKeys = 64;  // keys per tile
 
+// fmax over lanes l and l ^ 32 (the two halves of one 32x32 accumulator column).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int D, int NB, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   constexpr int QT = 128 * NB / G;        // positions per block
   constexpr int KS = D / 16;              // 16-dim steps of QK^T
   constexpr int DB = D / 32;              // 32-dim blocks of the output
-  constexpr int KPITCH = D + 8;           // LDS row pitch of K (bf16)
-  constexpr int VPITCH = kKeys + 4;       // LDS row pitch of V^T (bf16)
+  constexpr int PITCH = D + 8;            // LDS row pitch of K and V (bf16)
   constexpr int PIECES = D / 8;           // 16-byte pieces per K/V row
-  constexpr int LOADS = kKeys * PIECES / 256;
-  static_assert(QT >= 32 && QT % 32 == 0, "a 32-column block must stay within one head");
+  constexpr int ROWS = 256 / PIECES;      // rows one pass of the block fetches
+  constexpr int LOADS = kKeys / ROWS;     // passes per tile
+  constexpr int TILE = kKeys * PITCH;
+  static_assert(QT >= 16 && QT % 16 == 0, "each 16-lane group stays within one query head");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKeys * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VPITCH];
+  // [buffer][K or V][row * PITCH + dim]: two tiles in flight, one barrier per tile.
+  __shared__ __attribute__((aligned(16))) uint16_t kv[2][2][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -91,16 +99,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   const int kfull = P + q0 + 1;     // keys [0, kfull) are visible to every column
   const int ntiles = (kend + kKeys - 1) / kKeys;
 
-  // This wave's columns: NB blocks of 32 (query head hb, positions pos0..).
+  // This lane's columns: NB blocks of 32 (query head, position) pairs, head-major.
+  // Lanes l and l ^ 32 share a column and split its keys.
   const int half = lane >> 5;
   const int col = lane & 31;
   bf16x8 qb[NB][KS];
   int lim[NB], hb[NB], pos[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int c0 = wave * 32 * NB + nb * 32;
-    hb[nb] = c0 / QT;
-    pos[nb] = q0 + c0 % QT + col;
+    const int c = wave * 32 * NB + nb * 32 + col;
+    hb[nb] = c / QT;
+    pos[nb] = q0 + c % QT;
     const bool valid = pos[nb] <= qlast;
     lim[nb] = P + (valid ? pos[nb] : qlast);
     const uint16_t* qp =
@@ -114,42 +123,49 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     }
   }
 
+  // Tile fetch: thread -> (row lrow + ROWS * it, 16-byte piece lpc).  Page
+  // numbers are fetched one tile before the rows they locate.
+  const int lrow = tid / PIECES;
+  const int lpc = tid % PIECES;
   const int32_t* pt = p.page_table + (int64_t)r * p.pt_stride;
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
-  uint4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int kt) {
+  const uint16_t* kbase = p.k_cache + kvh * D + lpc * 8;
+  const uint16_t* vbase = p.v_cache + kvh * D + lpc * 8;
+  int pg[LOADS];
+  uint4 kr[LOADS], vr[LOADS];
+  auto fetch_pages = [&](int kt) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int piece = tid + 256 * it;
-      const int key = piece / PIECES;
-      const int pc = piece % PIECES;
-      const int kg = kt * kKeys + key;
+      const int kg = kt * kKeys + lrow + ROWS * it;
+      int page = -1;
       if (kg < kend) {
-        int page = pt[kg >> p.page_shift];
+        page = pt[kg >> p.page_shift];
         page = (page < 0 || (int64_t)page >= p.num_pages) ? 0 : page;
+      }
+      pg[it] = page;
+    }
+  };
+  auto fetch_rows = [&](int kt) {
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int kg = kt * kKeys + lrow + ROWS * it;
+      if (pg[it] >= 0) {
         const int64_t off =
-            ((int64_t)page * p.page_size + (kg & (p.page_size - 1))) * row_elems + kvh * D + pc * 8;
-        kreg[it] = ld16(p.k_cache + off);
-        vreg[it] = ld16(p.v_cache + off);
+            ((int64_t)pg[it] * p.page_size + (kg & (p.page_size - 1))) * row_elems;
+        kr[it] = ld16(kbase + off);
+        vr[it] = ld16(vbase + off);
       } else {
-        kreg[it] = make_uint4(0, 0, 0, 0);
-        vreg[it] = make_uint4(0, 0, 0, 0);
+        kr[it] = make_uint4(0, 0, 0, 0);
+        vr[it] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto store_tile = [&]() {
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int piece = tid + 256 * it;
-      const int key = piece / PIECES;
-      const int pc = piece % PIECES;
-      *reinterpret_cast<uint4*>(&Ks[key * KPITCH + pc * 8]) = kreg[it];
-      const uint32_t w[4] = {vreg[it].x, vreg[it].y, vreg[it].z, vreg[it].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(pc * 8 + 2 * e) * VPITCH + key] = (uint16_t)(w[e] & 0xffffu);
-        Vt[(pc * 8 + 2 * e + 1) * VPITCH + key] = (uint16_t)(w[e] >> 16);
-      }
+      const int o = (lrow + ROWS * it) * PITCH + lpc * 8;
+      *reinterpret_cast<uint4*>(&kv[buf][0][o]) = kr[it];
+      *reinterpret_cast<uint4*>(&kv[buf][1][o]) = vr[it];
     }
   };
 
@@ -164,14 +180,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) oacc[db][nb][v] = 0.f;
   }
+  const float c = p.scale_log2;
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  load_tile(0);
+  // Offsets of this lane's operand reads inside one tile (elements).
+  const int k_off = col * PITCH + 8 * half;
+  const int l16 = lane & 15;
+  const int v_off = (4 * half + (l16 >> 2)) * PITCH + 16 * ((lane >> 4) & 1) + 4 * (l16 & 3);
+
+  fetch_pages(0);
+  fetch_rows(0);
+  stash(0);
+  if (ntiles > 1) {
+    fetch_pages(1);
+    fetch_rows(1);
+    if (ntiles > 2) fetch_pages(2);
+  }
+
   for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < ntiles) load_tile(kt + 1);
-    const bool need_mask = (kt + 1) * kKeys > kfull;
+    __syncthreads();  // tile kt is in LDS; every wave is done with tile kt - 1
+    if (kt + 1 < ntiles) stash((kt + 1) & 1);
+    if (kt + 2 < ntiles) {
+      fetch_rows(kt + 2);
+      if (kt + 3 < ntiles) fetch_pages(kt + 3);
+    }
+    const uint16_t* Kt = kv[kt & 1][0];
+    const uint16_t* Vt = kv[kt & 1][1];
 
     // S^T tile: rows = 64 keys (two 32-key halves), columns = this wave's.
     f32x16 sacc[NB][2];
@@ -182,11 +216,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[nb][kh][v] = 0.f;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const uint4*>(&Ks[(kh * 32 + col) * KPITCH + 16 * ks + 8 * half]));
+      for (int kh = 0; kh < 2; ++kh) {
+        const bf16x8 a = as_bf16x8(ld16(&Kt[kh * 32 * PITCH + k_off + 16 * ks]));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           sacc[nb][kh] =
@@ -194,82 +227,81 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
       }
     }
 
-    // Scale, mask, tile max per column (the column's 64 keys are split
-    // between lanes l and l ^ 32).
+    // Causal mask, only on tiles that reach past the block's first column.
+    if ((kt + 1) * kKeys > kfull) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = kt * kKeys + kh * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
+            sacc[nb][kh][v] = key <= lim[nb] ? sacc[nb][kh][v] : kNegInf;
+          }
+    }
+
+    // Column maxima of the raw scores (the scale is positive), lazy rescale.
     bool grow = false;
     float mt[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float mx = kNegInf;
+      float a = fmaxf(sacc[nb][0][0], sacc[nb][1][0]);
+      float b = fmaxf(sacc[nb][0][1], sacc[nb][1][1]);
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = sacc[nb][kh][v] * p.scale_log2;
-          if (need_mask) {
-            const int key = kt * kKeys + kh * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-            x = key <= lim[nb] ? x : kNegInf;
-          }
-          sacc[nb][kh][v] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mt[nb] = mx;
-      grow |= mx > m[nb] + kTau;
+      for (int v = 2; v < 16; v += 2) {
+        a = fmaxf(a, fmaxf(sacc[nb][0][v], sacc[nb][1][v]));
+        b = fmaxf(b, fmaxf(sacc[nb][0][v + 1], sacc[nb][1][v + 1]));
+      }
+      mt[nb] = max_xor32(fmaxf(a, b)) * c;
+      grow |= mt[nb] > m[nb] + kTau;
     }
     if (__any(grow)) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float mn = fmaxf(m[nb], mt[nb]);
-        const float a = mn == kNegInf ? 0.f : fast_exp2(m[nb] - mn);
-        l[nb] *= a;
+        const float al = mn == kNegInf ? 1.f : fast_exp2(m[nb] - mn);
+        l[nb] *= al;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[db][nb][v] *= a;
+          for (int v = 0; v < 16; ++v) oacc[db][nb][v] *= al;
         m[nb] = mn;
       }
     }
 
-    // P = 2^(x - m) as bf16 B operands; one per (32-key half, 16-key step).
-    bf16x8 pb[NB][2][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float e[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            e[i] = fast_exp2(sacc[nb][kh][8 * u + i] - m[nb]);
-            l[nb] += e[i];
-          }
-          uint4 w;
-          w.x = pack_bf16x2(e[0], e[1]);
-          w.y = pack_bf16x2(e[2], e[3]);
-          w.z = pack_bf16x2(e[4], e[5]);
-          w.w = pack_bf16x2(e[6], e[7]);
-          pb[nb][kh][u] = as_bf16x8(w);
-        }
-
-    // O^T += V^T P^T.  Operand slot (half, i) of step (kh, u) holds key
-    // kh*32 + 16u + 8*(i/4) + 4*half + i%4 on both sides.
+    // P = 2^(s * c - m) in bf16 as the B operand of O^T += V^T P^T; the row
+    // sums add up the same rounded values.  Operand slot (half, i) of step
+    // (kh, u) holds key kh*32 + 16u + 8(i/4) + 4*half + i%4 on both sides;
+    // the V^T operand comes from two transposing LDS reads of 4 rows each.
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int koff = kh * 32 + 16 * u + 4 * half;
+        bf16x8 pb[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const float nm = -m[nb];
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float e0 = fast_exp2(__builtin_fmaf(sacc[nb][kh][8 * u + 2 * j], c, nm));
+            const float e1 = fast_exp2(__builtin_fmaf(sacc[nb][kh][8 * u + 2 * j + 1], c, nm));
+            w[j] = pack_bf16x2(e0, e1);
+            l[nb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, l[nb],
+                                                    false);
+          }
+          pb[nb] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        const uint16_t* vrow = Vt + (kh * 32 + 16 * u) * PITCH + v_off;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* vrow = &Vt[(db * 32 + col) * VPITCH + koff];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const s16x4 lo = lds_read_tr16(vrow + 32 * db);
+          const s16x4 hi = lds_read_tr16(vrow + 8 * PITCH + 32 * db);
+          const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            oacc[db][nb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb][kh][u], oacc[db][nb], 0, 0, 0);
+            oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb], oacc[db][nb], 0, 0, 0);
         }
       }
   }
@@ -326,7 +358,7 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   const int g = num_q_heads / num_kv_heads;
   if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
   const int nb = head_dim == 64 ? 2 : 1;
-  if (!(g == 1 || g == 2 || g == 4 || (g == 8 && nb == 2))) return PKV_EUNSUPPORTED;
+  if (!(g == 1 || g == 2 || g == 4 || g == 8)) return PKV_EUNSUPPORTED;
   const int qtile = 128 * nb / g;
   const int64_t n_qtiles = (max_q_len + qtile - 1) / qtile;
   const int64_t blocks = n_qtiles * num_seqs * num_kv_heads;
@@ -361,5 +393,6 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   }
   if (g == 1) return launch_prefill<128, 1, 1>(p, blocks, s);
   if (g == 2) return launch_prefill<128, 1, 2>(p, blocks, s);
-  return launch_prefill<128, 1, 4>(p, blocks, s);
+  if (g == 4) return launch_prefill<128, 1, 4>(p, blocks, s);
+  return launch_prefill<128, 1, 8>(p, blocks, s);
 }

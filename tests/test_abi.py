@@ -125,7 +125,7 @@ def _prefill(**kw):
     (dict(B=0), 1), (dict(B=-2), 1), (dict(T=-1), 1), (dict(maxq=0), 1), (dict(maxlen=0), 1),
     (dict(hq=33), 1), (dict(scale=0.0), 1), (dict(stride=62), 1), (dict(pages=0), 1),
     (dict(kc=FAKE + 8), 1),
-    (dict(ps=48), 2), (dict(d=80), 2), (dict(hq=128), 2), (dict(d=128, hq=64), 2),
+    (dict(ps=48), 2), (dict(d=80), 2), (dict(hq=128), 2), (dict(d=128, hq=256), 2),
     (dict(T=0, q=None), 0),
 ])
 def test_prefill_validation(kw, status):

@@ -29,6 +29,8 @@ CASES = [
     (8, 4, 128, 16, [20, 0, 0], [0, 45, 160]),
     (16, 4, 128, 64, [64, 7], [100, 1]),
     (8, 2, 64, 128, [1000, 0, 255], [65, 257, 2]),
+    (16, 2, 128, 16, [3, 0, 70], [90, 40, 17]),     # 8 query heads per KV head, 16-row tiles
+    (8, 1, 128, 32, [50], [33]),
 ]
 
 
