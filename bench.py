@@ -127,6 +127,8 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0):
     B, Hq, Hkv, d, ps = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
     split = pkv.pkv_decode_split_tokens(B, Hkv, w.max_seq_len, split_tokens) if is_decode else 0
     ws = pkv.decode_workspace(B, Hq, Hkv, d, w.max_seq_len, split_tokens) if is_decode else None
+    if not is_decode:
+        ws = torch.zeros(pkv.pkv_prefill_workspace_bytes(), dtype=torch.uint8, device="cuda")
     ws_ptr, ws_bytes = (0, 0) if ws is None else (ws.data_ptr(), ws.numel())
 
     # Pre-marshalled C calls: the timed loop only enqueues.
@@ -147,7 +149,8 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0):
             at = (c.q.data_ptr(), c.cu_seqlens_q.data_ptr(), c.prefix_lens.data_ptr(), B,
                   w.num_tokens, w.max_q_len, w.max_seq_len, c.k_cache.data_ptr(),
                   c.v_cache.data_ptr(), ps, c.num_pages, c.page_table.data_ptr(),
-                  c.page_table.shape[1], Hq, Hkv, d, w.scale, out.data_ptr(), stream)
+                  c.page_table.shape[1], Hq, Hkv, d, w.scale, out.data_ptr(), ws_ptr, ws_bytes,
+                  stream)
         calls.append((st, at, out))
     f_store = lib.pkv_store_kv
     f_attn = lib.pkv_paged_attn_decode if is_decode else lib.pkv_paged_attn_prefill

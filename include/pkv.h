@@ -181,8 +181,17 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
  *   softmax_scale: finite and > 0
  *   out          : [num_tokens, num_q_heads, head_dim] bf16; rows outside
  *                  every request are not written
+ *   workspace    : device memory, 16-byte aligned, at least
+ *                  pkv_prefill_workspace_bytes() bytes, caller-owned.  It
+ *                  holds the counter that hands work items to the resident
+ *                  blocks: it must be zero before its first use (e.g.
+ *                  allocated zeroed), and every call puts it back to zero
+ *                  before its kernel ends, so it is reused without clearing.
+ *                  Calls sharing one workspace must be ordered (one stream);
+ *                  concurrent calls need separate workspaces.
  *
- * num_tokens == 0 is a no-op returning PKV_OK.
+ * Returns PKV_ENOSPACE if workspace_bytes is too small.  num_tokens == 0 is a
+ * no-op returning PKV_OK (the workspace is not touched).
  */
 int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q,
                            const int32_t* prefix_lens, int32_t num_seqs,
@@ -192,7 +201,11 @@ int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q,
                            int64_t num_pages, const int32_t* page_table,
                            int32_t page_table_stride, int32_t num_q_heads,
                            int32_t num_kv_heads, int32_t head_dim,
-                           float softmax_scale, void* out, void* stream);
+                           float softmax_scale, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pkv_paged_attn_prefill needs (a small constant). */
+size_t pkv_prefill_workspace_bytes(void);
 
 #ifdef __cplusplus
 }

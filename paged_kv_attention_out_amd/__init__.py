@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     pkv_decode_workspace_bytes,
     pkv_paged_attn_decode,
     pkv_paged_attn_prefill,
+    pkv_prefill_workspace_bytes,
+    prefill_workspace,
     pkv_store_kv,
     strerror,
     version,

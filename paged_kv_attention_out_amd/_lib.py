@@ -34,7 +34,9 @@ SIGNATURES = {
         _i32, _i32, _i32, _f32, _i32, _c_void_p, _c_void_p, _size, _c_void_p]),
     "pkv_paged_attn_prefill": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p, _i32,
-        _i64, _c_void_p, _i32, _i32, _i32, _i32, _f32, _c_void_p, _c_void_p]),
+        _i64, _c_void_p, _i32, _i32, _i32, _i32, _f32, _c_void_p, _c_void_p, _size,
+        _c_void_p]),
+    "pkv_prefill_workspace_bytes": (_size, []),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -154,12 +156,36 @@ def pkv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     return out
 
 
+def pkv_prefill_workspace_bytes() -> int:
+    return int(lib().pkv_prefill_workspace_bytes())
+
+
+_PREFILL_WS = {}
+
+
+def prefill_workspace(device: torch.device, stream: int) -> torch.Tensor:
+    """A zeroed prefill workspace for one (device, stream).
+
+    Every prefill call leaves its workspace zeroed again, so one buffer serves
+    all calls that are ordered on that stream."""
+    key = (device.index, stream)
+    ws = _PREFILL_WS.get(key)
+    if ws is None:
+        ws = torch.zeros(pkv_prefill_workspace_bytes(), dtype=torch.uint8, device=device)
+        _PREFILL_WS[key] = ws
+    return ws
+
+
 def pkv_paged_attn_prefill(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
                            prefix_lens: torch.Tensor, max_q_len: int, max_seq_len: int,
                            k_cache: torch.Tensor, v_cache: torch.Tensor,
                            page_table: torch.Tensor, softmax_scale: float,
-                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Causal prefill with prefix; q ``[T, Hq, d]`` -> out ``[T, Hq, d]``."""
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal prefill with prefix; q ``[T, Hq, d]`` -> out ``[T, Hq, d]``.
+
+    ``workspace`` (uint8, zero before its first use) defaults to one buffer
+    per (device, stream)."""
     _dev(q, torch.bfloat16, "q")
     _dev(k_cache, torch.bfloat16, "k_cache")
     _dev(v_cache, torch.bfloat16, "v_cache")
@@ -172,8 +198,13 @@ def pkv_paged_attn_prefill(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     _dev(out, torch.bfloat16, "out")
+    stream = _stream(q)
+    if workspace is None:
+        workspace = prefill_workspace(q.device, stream)
+    _dev(workspace, torch.uint8, "workspace")
     _check(lib().pkv_paged_attn_prefill(
         _ptr(q), _ptr(cu_seqlens_q), _ptr(prefix_lens), B, T, max_q_len, max_seq_len,
         _ptr(k_cache), _ptr(v_cache), ps, num_pages, _ptr(page_table), page_table.shape[1], Hq,
-        Hkv, d, softmax_scale, _ptr(out), _stream(q)), "pkv_paged_attn_prefill")
+        Hkv, d, softmax_scale, _ptr(out), _ptr(workspace), workspace.numel(), stream),
+        "pkv_paged_attn_prefill")
     return out

@@ -6,10 +6,18 @@
 // sequence length - cached length).  New token i of request r is at
 // absolute position P_r + i and sees keys 0 .. P_r + i.
 //
-// Work unit = one 256-thread block per (request, KV head, query tile).  The
-// block's 128*NB "columns" are (query head of the group, position) pairs,
-// head-major, so the g query heads that share a KV head reuse every K/V tile
-// staged in LDS; each wave owns NB blocks of 32 columns.
+// Work item = (query tile, request, KV head).  The block's 128*NB "columns"
+// are (query head of the group, position) pairs, head-major, so the g query
+// heads that share a KV head reuse every K/V tile staged in LDS; each wave
+// owns NB blocks of 32 columns.
+//
+// The grid is persistent: as many 256-thread blocks as fit on the device at
+// once, each pulling items from a counter in the caller's workspace, latest
+// query tiles (the longest key ranges) first.  The hardware dispatcher starts
+// blocks strictly in grid order, so a grid of one block per item leaves CUs
+// idle behind long-running blocks; pulling keeps every resident block busy
+// until the items run out.  The block that draws the last ticket puts the
+// counter back to zero, ready for the next call on the same workspace.
 //
 // Per 64-key tile:
 //   * K and V rows are fetched through the page table into registers one
@@ -23,6 +31,9 @@
 //     accumulator layout of S^T is already the B operand layout of
 //     O^T += V^T P^T, with the key order permuted identically on both sides.
 // Arithmetic per visible (query, key) pair: 4 * head_dim flops on MFMA.
+
+#include <algorithm>
+#include <atomic>
 
 #include "pkv_common.h"
 
@@ -38,6 +49,7 @@ struct PrefillParams {
   const uint16_t* v_cache;
   const int32_t* page_table;
   uint16_t* out;
+  uint32_t* counter;  // work-item counter (zero on entry, zero again on exit)
   int64_t num_pages;
   int32_t num_seqs;
   int32_t num_tokens;
@@ -49,9 +61,11 @@ struct PrefillParams {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t n_qtiles;
+  int32_t n_items;
   float scale_log2;
 };
 
+constexpr size_t kPrefillWorkspaceBytes = 256;  // one counter, padded
 constexpr float kTau = 8.0f;
 constexpr int kKeys = 64;  // keys per tile
 
@@ -62,27 +76,58 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+template <int D, int NB, int G, typename KV>
+__device__ __forceinline__ void attend_item(const PrefillParams& p, int item, int rk_all, int tid,
+                                            int lane, int wave, KV& kv);
+
 template <int D, int NB, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
-  constexpr int QT = 128 * NB / G;        // positions per block
+  constexpr int QT = 128 * NB / G;
+  constexpr int TILE = kKeys * (D + 8);
+  static_assert(QT >= 16 && QT % 16 == 0, "each 16-lane group stays within one query head");
+
+  // [buffer][K or V][row * pitch + dim]: two tiles in flight, one barrier per tile.
+  __shared__ __attribute__((aligned(16))) uint16_t kv[2][2][TILE];
+  __shared__ uint32_t item_slot[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rk_all = p.num_seqs * p.num_kv_heads;
+
+  // Tickets are compared unsigned, so even a counter left non-zero by a
+  // misuse only ever yields item numbers inside [0, n_items).
+  if (tid == 0) item_slot[0] = atomicAdd(p.counter, 1u);
+  __syncthreads();
+  int par = 0;
+  // readfirstlane: the item is block-uniform, so its geometry stays scalar.
+  for (uint32_t item = uniform(item_slot[0]);; item = uniform(item_slot[par])) {
+    if (item >= (uint32_t)p.n_items) {
+      // Every block draws exactly one ticket past the end; the last such
+      // ticket is drawn after all others, so its holder resets the counter.
+      if (tid == 0 && item - (uint32_t)p.n_items == gridDim.x - 1) atomicExch(p.counter, 0u);
+      break;
+    }
+    if (tid == 0) item_slot[par ^ 1] = atomicAdd(p.counter, 1u);
+    par ^= 1;
+    attend_item<D, NB, G>(p, (int)item, rk_all, tid, lane, wave, kv);
+    __syncthreads();  // LDS tiles free; the next item number is visible
+  }
+}
+
+template <int D, int NB, int G, typename KV>
+__device__ __forceinline__ void attend_item(const PrefillParams& p, int item, int rk_all, int tid,
+                                            int lane, int wave, KV& kv) {
+  constexpr int QT = 128 * NB / G;        // positions per item
   constexpr int KS = D / 16;              // 16-dim steps of QK^T
   constexpr int DB = D / 32;              // 32-dim blocks of the output
   constexpr int PITCH = D + 8;            // LDS row pitch of K and V (bf16)
   constexpr int PIECES = D / 8;           // 16-byte pieces per K/V row
   constexpr int ROWS = 256 / PIECES;      // rows one pass of the block fetches
   constexpr int LOADS = kKeys / ROWS;     // passes per tile
-  constexpr int TILE = kKeys * PITCH;
-  static_assert(QT >= 16 && QT % 16 == 0, "each 16-lane group stays within one query head");
 
-  // [buffer][K or V][row * PITCH + dim]: two tiles in flight, one barrier per tile.
-  __shared__ __attribute__((aligned(16))) uint16_t kv[2][2][TILE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int rk_all = p.num_seqs * p.num_kv_heads;
-  const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / rk_all);  // longest tiles first
-  const int rk = (int)(blockIdx.x % rk_all);
+  const int qt = p.n_qtiles - 1 - item / rk_all;  // longest key ranges first
+  const int rk = item % rk_all;
   const int kvh = rk % p.num_kv_heads;
   const int r = rk / p.num_kv_heads;
 
@@ -125,33 +170,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 
   // Tile fetch: thread -> (row lrow + ROWS * it, 16-byte piece lpc).  Page
   // numbers are fetched one tile before the rows they locate.
-  const int lrow = tid / PIECES;
+  // The empty asm makes lrow opaque per item, so the compiler does not hoist
+  // item-invariant address arithmetic of the first tiles out of the item loop
+  // (where it would stay live through the whole tile loop and spill).
+  int lrow = tid / PIECES;
+  asm volatile("" : "+v"(lrow));
   const int lpc = tid % PIECES;
   const int32_t* pt = p.page_table + (int64_t)r * p.pt_stride;
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
   const uint16_t* kbase = p.k_cache + kvh * D + lpc * 8;
   const uint16_t* vbase = p.v_cache + kvh * D + lpc * 8;
-  int pg[LOADS];
+  int pg[LOADS] = {};
   uint4 kr[LOADS], vr[LOADS];
+  // Raw page numbers are checked only where they are used, a tile later, so
+  // that their loads never hold up the wave.
   auto fetch_pages = [&](int kt) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int kg = kt * kKeys + lrow + ROWS * it;
-      int page = -1;
-      if (kg < kend) {
-        page = pt[kg >> p.page_shift];
-        page = (page < 0 || (int64_t)page >= p.num_pages) ? 0 : page;
-      }
-      pg[it] = page;
+      if (kg < kend) pg[it] = pt[kg >> p.page_shift];
     }
   };
   auto fetch_rows = [&](int kt) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int kg = kt * kKeys + lrow + ROWS * it;
-      if (pg[it] >= 0) {
-        const int64_t off =
-            ((int64_t)pg[it] * p.page_size + (kg & (p.page_size - 1))) * row_elems;
+      if (kg < kend) {
+        const int64_t page = (pg[it] < 0 || pg[it] >= p.num_pages) ? 0 : pg[it];
+        const int64_t off = (page * p.page_size + (kg & (p.page_size - 1))) * row_elems;
         kr[it] = ld16(kbase + off);
         vr[it] = ld16(vbase + off);
       } else {
@@ -326,12 +372,40 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   }
 }
 
+// Resident blocks per CU of one instantiation times the CU count of the
+// current device, computed once per (device, instantiation).
 template <int D, int NB, int G>
-int launch_prefill(const PrefillParams& p, int64_t blocks, hipStream_t s) {
-  return pkv_host::launch(prefill_kernel<D, NB, G>, dim3((unsigned)blocks), dim3(256), s, p);
+int resident_blocks() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(prefill_kernel<D, NB, G>), 256, 0) != hipSuccess)
+    return 0;
+  const int n = cus * per_cu;
+  if (n > 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int D, int NB, int G>
+int launch_prefill(PrefillParams& p, hipStream_t s) {
+  const int resident = resident_blocks<D, NB, G>();
+  if (resident <= 0) return PKV_EHIP;
+  const int grid = (int)std::min<int64_t>(p.n_items, resident);
+  return pkv_host::launch(prefill_kernel<D, NB, G>, dim3((unsigned)grid), dim3(256), s, p);
 }
 
 }  // namespace
+
+extern "C" size_t pkv_prefill_workspace_bytes(void) { return kPrefillWorkspaceBytes; }
 
 extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q,
                                       const int32_t* prefix_lens, int32_t num_seqs,
@@ -341,16 +415,19 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
                                       int64_t num_pages, const int32_t* page_table,
                                       int32_t page_table_stride, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
-                                      float softmax_scale, void* out, void* stream) {
+                                      float softmax_scale, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   using namespace pkv_host;
   if (num_seqs < 0 || num_tokens < 0) return PKV_EINVAL;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return PKV_EINVAL;
   if (!finite_positive(softmax_scale)) return PKV_EINVAL;
   if (num_tokens == 0) return PKV_OK;
   if (num_seqs == 0 || max_q_len <= 0 || max_seq_len <= 0) return PKV_EINVAL;
-  if (!q || !cu_seqlens_q || !prefix_lens || !k_cache || !v_cache || !page_table || !out)
+  if (!q || !cu_seqlens_q || !prefix_lens || !k_cache || !v_cache || !page_table || !out ||
+      !workspace)
     return PKV_EINVAL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
     return PKV_EINVAL;
   if (num_pages <= 0 || page_table_stride <= 0) return PKV_EINVAL;
   if (!is_pow2_page(page_size)) return PKV_EUNSUPPORTED;
@@ -359,10 +436,11 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
   const int nb = head_dim == 64 ? 2 : 1;
   if (!(g == 1 || g == 2 || g == 4 || g == 8)) return PKV_EUNSUPPORTED;
+  if (workspace_bytes < kPrefillWorkspaceBytes) return PKV_ENOSPACE;
   const int qtile = 128 * nb / g;
   const int64_t n_qtiles = (max_q_len + qtile - 1) / qtile;
-  const int64_t blocks = n_qtiles * num_seqs * num_kv_heads;
-  if (blocks > INT32_MAX || (int64_t)num_seqs * num_kv_heads > INT32_MAX) return PKV_EINVAL;
+  const int64_t n_items = n_qtiles * num_seqs * num_kv_heads;
+  if (n_items >= INT32_MAX / 2) return PKV_EINVAL;
 
   PrefillParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -372,6 +450,7 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   p.v_cache = static_cast<const uint16_t*>(v_cache);
   p.page_table = page_table;
   p.out = static_cast<uint16_t*>(out);
+  p.counter = static_cast<uint32_t*>(workspace);
   p.num_pages = num_pages;
   p.num_seqs = num_seqs;
   p.num_tokens = num_tokens;
@@ -383,16 +462,17 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.n_qtiles = (int32_t)n_qtiles;
+  p.n_items = (int32_t)n_items;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (head_dim == 64) {
-    if (g == 1) return launch_prefill<64, 2, 1>(p, blocks, s);
-    if (g == 2) return launch_prefill<64, 2, 2>(p, blocks, s);
-    if (g == 4) return launch_prefill<64, 2, 4>(p, blocks, s);
-    return launch_prefill<64, 2, 8>(p, blocks, s);
+    if (g == 1) return launch_prefill<64, 2, 1>(p, s);
+    if (g == 2) return launch_prefill<64, 2, 2>(p, s);
+    if (g == 4) return launch_prefill<64, 2, 4>(p, s);
+    return launch_prefill<64, 2, 8>(p, s);
   }
-  if (g == 1) return launch_prefill<128, 1, 1>(p, blocks, s);
-  if (g == 2) return launch_prefill<128, 1, 2>(p, blocks, s);
-  if (g == 4) return launch_prefill<128, 1, 4>(p, blocks, s);
-  return launch_prefill<128, 1, 8>(p, blocks, s);
+  if (g == 1) return launch_prefill<128, 1, 1>(p, s);
+  if (g == 2) return launch_prefill<128, 1, 2>(p, s);
+  if (g == 4) return launch_prefill<128, 1, 4>(p, s);
+  return launch_prefill<128, 1, 8>(p, s);
 }

@@ -112,16 +112,17 @@ def test_decode_workspace_sizes():
 def _prefill(**kw):
     a = dict(q=FAKE, cu=FAKE, prefix=FAKE, B=4, T=100, maxq=50, maxlen=1000, kc=FAKE, vc=FAKE,
              ps=16, pages=100, pt=FAKE, stride=64, hq=32, hkv=8, d=64, scale=0.125, out=FAKE,
-             stream=None)
+             ws=FAKE, wsb=256, stream=None)
     a.update(kw)
     return pkv.lib().pkv_paged_attn_prefill(
         a["q"], a["cu"], a["prefix"], a["B"], a["T"], a["maxq"], a["maxlen"], a["kc"], a["vc"],
         a["ps"], a["pages"], a["pt"], a["stride"], a["hq"], a["hkv"], a["d"], a["scale"],
-        a["out"], a["stream"])
+        a["out"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(cu=None), 1), (dict(prefix=None), 1), (dict(out=None), 1),
+    (dict(ws=None), 1), (dict(ws=FAKE + 4), 1), (dict(wsb=0), 3), (dict(wsb=255), 3),
     (dict(B=0), 1), (dict(B=-2), 1), (dict(T=-1), 1), (dict(maxq=0), 1), (dict(maxlen=0), 1),
     (dict(hq=33), 1), (dict(scale=0.0), 1), (dict(stride=62), 1), (dict(pages=0), 1),
     (dict(kc=FAKE + 8), 1),
@@ -130,6 +131,10 @@ def _prefill(**kw):
 ])
 def test_prefill_validation(kw, status):
     assert _prefill(**kw) == status
+
+
+def test_prefill_workspace_size():
+    assert 4 <= pkv.pkv_prefill_workspace_bytes() <= 4096
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

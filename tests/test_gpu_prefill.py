@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from oracle import paged_attention as orc
+import paged_kv_attention_out_amd as pkv
 from paged_kv_attention_out_amd import inputs
 
 from gpu_helpers import assert_close, f64, host_pools, run_decode, run_prefill, run_store
@@ -106,3 +107,24 @@ def test_decode_equals_one_row_prefill():
     torch.cuda.synchronize()
     assert np.abs(dec - pre).max() <= 2e-2
     assert np.abs(dec - pre).mean() <= 2e-3
+
+
+def test_prefill_workspace_returns_to_zero():
+    """The work counter goes back to zero at the end of every call, so one
+    workspace serves calls of any size in a row (more and fewer work items
+    than resident blocks)."""
+    ws = torch.zeros(pkv.pkv_prefill_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    shapes = [(1, 4, 4, 64, 16, [3], [5]),                       # one work item
+              (3, 8, 2, 64, 16, [40, 0, 300], [500, 64, 1]),
+              (2, 8, 1, 128, 32, [0, 9], [700, 31])]
+    for i, (B, hq, hkv, d, ps, prefix, qlens) in enumerate(shapes):
+        print(f"workspace call {i}: hq={hq} hkv={hkv} d={d} qlens={qlens}", flush=True)
+        w = inputs.build_prefill(B, hq, hkv, d, ps, prefix, qlens, seed=50 + i, device="cuda")
+        ref = _oracle(w)
+        run_store(w)
+        out = pkv.pkv_paged_attn_prefill(w.q, w.cu_seqlens_q, w.prefix_lens, w.max_q_len,
+                                         w.max_seq_len, w.k_cache, w.v_cache, w.page_table,
+                                         w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0, f"call {i} left the counter non-zero"
+        assert_close(f64(out), ref, f"workspace call {i}")
