@@ -62,6 +62,9 @@ struct PrefillParams {
   int32_t num_kv_heads;
   int32_t n_qtiles;
   int32_t n_items;
+  uint32_t num_pages_u32;  // min(num_pages, 2^31 - 1): page numbers at or above it read page 0
+  uint32_t page_bytes;     // bytes per page of one pool (K or V)
+  uint32_t row_bytes;      // bytes per token row (all KV heads)
   float scale_log2;
 };
 
@@ -168,8 +171,11 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
     }
   }
 
-  // Tile fetch: thread -> (row lrow + ROWS * it, 16-byte piece lpc).  Page
-  // numbers are fetched one tile before the rows they locate.
+  // Tile fetch: thread -> (row lrow + ROWS * it, 16-byte piece lpc).  Rows
+  // past the last key read are clamped onto it (always a valid row of the
+  // request; those keys are masked), so every load is unconditional.  Page
+  // numbers are fetched a tile before the rows they locate and checked only
+  // where they are used, so their loads never hold up the wave.
   // The empty asm makes lrow opaque per item, so the compiler does not hoist
   // item-invariant address arithmetic of the first tiles out of the item loop
   // (where it would stay live through the whole tile loop and spill).
@@ -177,33 +183,28 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
   asm volatile("" : "+v"(lrow));
   const int lpc = tid % PIECES;
   const int32_t* pt = p.page_table + (int64_t)r * p.pt_stride;
-  const int64_t row_elems = (int64_t)p.num_kv_heads * D;
-  const uint16_t* kbase = p.k_cache + kvh * D + lpc * 8;
-  const uint16_t* vbase = p.v_cache + kvh * D + lpc * 8;
-  int pg[LOADS] = {};
+  const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (kvh * D + lpc * 8) * 2;
+  const int64_t v_minus_k = reinterpret_cast<const char*>(p.v_cache) -
+                            reinterpret_cast<const char*>(p.k_cache);
+  const int klast = kend - 1;
+  const int pmask = p.page_size - 1;
+  int pg[LOADS];
   uint4 kr[LOADS], vr[LOADS];
-  // Raw page numbers are checked only where they are used, a tile later, so
-  // that their loads never hold up the wave.
   auto fetch_pages = [&](int kt) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int kg = kt * kKeys + lrow + ROWS * it;
-      if (kg < kend) pg[it] = pt[kg >> p.page_shift];
+      const int kg = min(kt * kKeys + lrow + ROWS * it, klast);
+      pg[it] = pt[kg >> p.page_shift];
     }
   };
   auto fetch_rows = [&](int kt) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int kg = kt * kKeys + lrow + ROWS * it;
-      if (kg < kend) {
-        const int64_t page = (pg[it] < 0 || pg[it] >= p.num_pages) ? 0 : pg[it];
-        const int64_t off = (page * p.page_size + (kg & (p.page_size - 1))) * row_elems;
-        kr[it] = ld16(kbase + off);
-        vr[it] = ld16(vbase + off);
-      } else {
-        kr[it] = make_uint4(0, 0, 0, 0);
-        vr[it] = make_uint4(0, 0, 0, 0);
-      }
+      const int kg = min(kt * kKeys + lrow + ROWS * it, klast);
+      const uint32_t page = (uint32_t)pg[it] < p.num_pages_u32 ? (uint32_t)pg[it] : 0u;
+      const char* kp = kbase + (uint64_t)page * p.page_bytes + __umul24(kg & pmask, p.row_bytes);
+      kr[it] = ld16(kp);
+      vr[it] = ld16(kp + v_minus_k);
     }
   };
   auto stash = [&](int buf) {
@@ -273,17 +274,21 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
       }
     }
 
-    // Causal mask, only on tiles that reach past the block's first column.
+    // Causal mask, only on tiles that reach past the block's first column:
+    // accumulator slot (kh, v) holds key kt*64 + 4*half + kh*32 + 8(v/4) + v%4,
+    // so each slot compares a compile-time offset with a per-lane threshold.
     if ((kt + 1) * kKeys > kfull) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
+        const int thr = lim[nb] - kt * kKeys - 4 * half;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int key = kt * kKeys + kh * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-            sacc[nb][kh][v] = key <= lim[nb] ? sacc[nb][kh][v] : kNegInf;
+            const int off = kh * 32 + (v >> 2) * 8 + (v & 3);
+            sacc[nb][kh][v] = off <= thr ? sacc[nb][kh][v] : kNegInf;
           }
+      }
     }
 
     // Column maxima of the raw scores (the scale is positive), lazy rescale.
@@ -441,6 +446,11 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   const int64_t n_qtiles = (max_q_len + qtile - 1) / qtile;
   const int64_t n_items = n_qtiles * num_seqs * num_kv_heads;
   if (n_items >= INT32_MAX / 2) return PKV_EINVAL;
+  // Row addresses are formed from a 32-bit page size and a 24-bit in-page
+  // offset: pages of one pool must stay below 4 GiB.
+  const int64_t page_bytes = (int64_t)page_size * num_kv_heads * head_dim * 2;
+  if (page_bytes >= ((int64_t)1 << 32) || (int64_t)num_kv_heads * head_dim * 2 >= (1 << 24))
+    return PKV_EUNSUPPORTED;
 
   PrefillParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -463,6 +473,9 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   p.num_kv_heads = num_kv_heads;
   p.n_qtiles = (int32_t)n_qtiles;
   p.n_items = (int32_t)n_items;
+  p.num_pages_u32 = (uint32_t)std::min<int64_t>(num_pages, INT32_MAX);
+  p.row_bytes = (uint32_t)(num_kv_heads * head_dim * 2);
+  p.page_bytes = (uint32_t)page_bytes;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (head_dim == 64) {
