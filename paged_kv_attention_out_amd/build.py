@@ -24,8 +24,11 @@ ARCH = "gfx950"
 # -packed-fp32-ops: no packed fp32 VALU instructions are emitted.
 # -fno-honor-nans: the kernels mask with -inf and never read unowned slots, so
 # fmaxf over MFMA results needs no NaN-quieting pass (one VALU op per score).
+# -amdgpu-mfma-vgpr-form: MFMA accumulators stay in VGPRs; the softmax reads
+# every score, and accumulators in AGPRs would cost a VALU move per read.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fno-honor-nans",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

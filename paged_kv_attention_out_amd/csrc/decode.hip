@@ -422,6 +422,13 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   }
 }
 
+// The loads of a batch of splits do not depend on the request length: the
+// partials of every split up to the host bound are read at once (in bounds
+// of the workspace; stale entries past the request's last split are never
+// used), so the kernel costs one memory round trip for the length and one
+// for the partials, not a chain of them.
+constexpr int kCombineBatch = 16;  // splits whose o rows are in flight together
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   constexpr int DPL = D / 64;  // output dims per lane
@@ -431,54 +438,65 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int r = (int)(rh / p.num_q_heads);
   const int qh = (int)(rh % p.num_q_heads);
   const int kvh = qh / G, h = qh % G;
-  int n = uniform(p.seq_lens[r]);
+  const int nsm = p.n_split_max;
+  const int64_t sbase = ((int64_t)r * p.num_kv_heads + kvh) * nsm;  // split 0
+  const float* om = p.ws_m + sbase * G + h;
+  const float* ol = p.ws_l + sbase * G + h;
+  const float* oo = p.ws_o + sbase * G * D + (int64_t)h * D + lane;
+
+  int n = p.seq_lens[r];
+  // First batch of partials, issued together with the length.
+  float mv = lane < nsm ? om[(int64_t)lane * G] : kNegInf;
+  float lv = lane < nsm ? ol[(int64_t)lane * G] : 0.f;
+  float v[kCombineBatch][DPL];
+#pragma unroll
+  for (int k = 0; k < kCombineBatch; ++k)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) v[k][i] = k < nsm ? oo[(int64_t)k * G * D + 64 * i] : 0.f;
+
+  n = uniform(n);
   n = n > p.max_seq_len ? p.max_seq_len : n;
   if (n <= 0) return;
   const int ns = (n + p.split - 1) / p.split;
   if (ns == 1) return;  // written by the split kernel
-  const int64_t sbase = ((int64_t)r * p.num_kv_heads + kvh) * p.n_split_max;  // split 0
 
-  // Global max over the splits (lane s reads split s, 64 at a time).
+  // Global max over the splits (lane s holds split s, 64 at a time).
   float M = kNegInf;
   for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s = s0 + lane;
-    float mv = s < ns ? p.ws_m[(sbase + s) * G + h] : kNegInf;
+    float x = s0 + lane < ns ? (s0 == 0 ? mv : om[(int64_t)(s0 + lane) * G]) : kNegInf;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off));
-    M = fmaxf(M, mv);
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    M = fmaxf(M, x);
   }
   float L = 0.f, acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   for (int s0 = 0; s0 < ns; s0 += 64) {
     const int s = s0 + lane;
-    const float w = s < ns ? fast_exp2(p.ws_m[(sbase + s) * G + h] - M) : 0.f;
-    float t = s < ns ? p.ws_l[(sbase + s) * G + h] * w : 0.f;
+    const float ms = s < ns ? (s0 == 0 ? mv : om[(int64_t)s * G]) : kNegInf;
+    const float w = s < ns ? fast_exp2(ms - M) : 0.f;
+    float t = s < ns ? (s0 == 0 ? lv : ol[(int64_t)s * G]) * w : 0.f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
     L += t;
-    // lane = output dim; eight splits' loads in flight per step
+    // lane = output dim; the weights of the 64 splits are broadcast by readlane
     const int cnt = min(64, ns - s0);
-    int k = 0;
-    for (; k + 8 <= cnt; k += 8) {
-      float v[8][DPL];
+    for (int k0 = 0; k0 < cnt; k0 += kCombineBatch) {
+      if (s0 + k0 != 0) {  // later batches: load now (the first came with the length)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+        for (int k = 0; k < kCombineBatch; ++k)
 #pragma unroll
-        for (int i = 0; i < DPL; ++i)
-          v[u][i] = p.ws_o[((sbase + s0 + k + u) * G + h) * D + lane + 64 * i];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k + u));
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(v[u][i], wk, acc[i]);
+          for (int i = 0; i < DPL; ++i)
+            v[k][i] = k0 + k < cnt ? oo[(int64_t)(s0 + k0 + k) * G * D + 64 * i] : 0.f;
       }
-    }
-    for (; k < cnt; ++k) {
-      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
-      for (int i = 0; i < DPL; ++i)
-        acc[i] = fmaf(p.ws_o[((sbase + s0 + k) * G + h) * D + lane + 64 * i], wk, acc[i]);
+      for (int k = 0; k < kCombineBatch; ++k) {
+        if (k0 + k < cnt) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + k));
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) acc[i] = fmaf(v[k][i], wk, acc[i]);
+        }
+      }
     }
   }
   uint16_t* out = p.out + rh * D;
