@@ -144,32 +144,54 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   __shared__ __attribute__((aligned(16))) uint16_t vlds[NBUF * 16 * VPITCH];
 
   const int lane = threadIdx.x;
-  // unit = (split * B + r) * Hkv + kvh.  The KV heads of one (request,
-  // split) are dispatched together and sweep the same pages, so between
-  // them they read whole rows of each page; split-major order puts the
-  // splits that may be empty (past a short request's end) last.
-  const uint32_t unit = blockIdx.x;  // one wave per block
-  const uint32_t sr = unit / (uint32_t)p.num_kv_heads;
+  // Block -> unit: rank = block / Hkv walks the (request, split) pairs that
+  // exist -- request-major, each request with max(ceil(n / split), 1)
+  // splits -- so every block of the grid past the last pair sits at its end
+  // and the dispatcher starts real units first.  The KV head is the fastest
+  // index: the heads of one (request, split) sweep the same pages together.
+  // It rotates from one rank to the next because blocks land on the 8 XCDs
+  // round-robin: every XCD then sees every head's offset within the page rows.
+  const uint32_t rank = blockIdx.x / (uint32_t)p.num_kv_heads;
 #ifdef PKV_DECODE_NO_ROTATE
-  const int kvh = (int)(unit % (uint32_t)p.num_kv_heads);
+  const int kvh = (int)(blockIdx.x % (uint32_t)p.num_kv_heads);
 #else
-  // Rotate the heads over the dispatch slots from one (request, split) to
-  // the next: blocks land on XCDs round-robin, so every XCD sees every
-  // head's offset within the page rows instead of always the same one.
-  const int kvh = (int)((unit + sr) % (uint32_t)p.num_kv_heads);
+  const int kvh = (int)((blockIdx.x + rank) % (uint32_t)p.num_kv_heads);
 #endif
-  const int r = (int)(sr % (uint32_t)p.num_seqs);
-  const int split = (int)(sr / (uint32_t)p.num_seqs);
-  if (split >= p.n_split_max) return;
+  int r = -1, split = 0, n = 0;
+  {
+    int base = 0;  // pairs of the requests before this chunk of 64
+    for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
+      const int rr = c0 + lane;
+      int len = 0, cnt = 0;
+      if (rr < p.num_seqs) {
+        len = min(p.seq_lens[rr], p.max_seq_len);
+        cnt = len <= 0 ? 1 : (len + p.split - 1) / p.split;
+      }
+      int inc = cnt;  // inclusive scan over the lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(inc, off);
+        if (lane >= off) inc += t;
+      }
+      const int total = uniform(__shfl(inc, 63));
+      if ((int)rank < base + total) {
+        const int rel = (int)rank - base;
+        const uint64_t hit = __ballot(rel >= inc - cnt && rel < inc);
+        const int lr = (int)__builtin_ctzll(hit);
+        r = c0 + lr;
+        split = rel - uniform(__shfl(inc - cnt, lr));
+        n = uniform(__shfl(len, lr));
+        break;
+      }
+      base += total;
+    }
+  }
+  if (r < 0) return;  // past the last pair
   const int64_t rk = (int64_t)r * p.num_kv_heads + kvh;
   const int j = lane & 15;  // token within the group / score column
   const int c = lane >> 4;  // 16-byte piece within each 64-byte block / token quad
   const int hcol = j % G;   // query head of this lane's score column
   const int t_begin = split * p.split;
-
-  // Issue every load that does not depend on the length first: the length
-  // itself, the Q fragments and the split's first page-table window.
-  int n = uniform(p.seq_lens[r]);
 
   // Q^T fragments (B operand): column j holds head kvh*G + j % G.
   bf16x8 qb[KCH];
@@ -194,7 +216,6 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   load_window(t_begin >> p.page_shift);
 
   uint16_t* out_rk = p.out + ((int64_t)r * p.num_q_heads + (int64_t)kvh * G) * D;
-  n = n > p.max_seq_len ? p.max_seq_len : n;
   if (n <= 0) {
     if (split == 0)
       for (int i = lane; i < G * D / 8; i += 64)
@@ -202,7 +223,6 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
     return;
   }
   const int ns = (n + p.split - 1) / p.split;
-  if (split >= ns) return;
   const int t_end = min(n, t_begin + p.split);
 
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
