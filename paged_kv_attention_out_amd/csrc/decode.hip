@@ -40,7 +40,7 @@
 #include "pkv_common.h"
 
 #ifndef PKV_DECODE_NBUF_D64
-#define PKV_DECODE_NBUF_D64 4
+#define PKV_DECODE_NBUF_D64 8
 #endif
 #ifndef PKV_DECODE_NBUF_D128
 #define PKV_DECODE_NBUF_D128 4
