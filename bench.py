@@ -71,12 +71,23 @@ def prefill_bytes(w) -> int:
     return kv + qo
 
 
+def source_digest(path: str) -> str:
+    """sha256 of a kernel source with comments and blank space removed, so a
+    change to comments alone does not invalidate counters taken on it."""
+    import hashlib
+    import re
+
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def measured_traffic(workload: str):
     """HBM bytes per decode call measured with rocprofv3 counters
     (profiles/traffic.txt), or None when the kernel source has changed since
     the counters were taken."""
-    import hashlib
-
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", "traffic.txt")
     if not os.path.exists(path):
@@ -88,7 +99,7 @@ def measured_traffic(workload: str):
         if wl != workload:
             continue
         try:
-            cur = hashlib.sha256(open(os.path.join(root, src), "rb").read()).hexdigest()
+            cur = source_digest(os.path.join(root, src))
         except OSError:
             return None
         return int(fetch) + int(write) if cur.startswith(sha) else None

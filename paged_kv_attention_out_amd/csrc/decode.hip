@@ -8,28 +8,18 @@
 // decode_split_kernel -- one wavefront per (request r, KV head kvh, split s).
 //   A split is `split` consecutive tokens; a request with n tokens has
 //   ceil(n/split) splits.  The wave walks its tokens 16 at a time ("groups"):
-//   * Lane l holds token j = l % 16 of the group and, for each 32-dim block
-//     kk, the 8 dims 32*kk + 8*c .. +7 with c = l / 16.  Those are the B
-//     operands of D/32 MFMA 16x16x32 bf16 instructions computing S = Q K^T
-//     (the contraction order over head dims is a free permutation; Q uses the
-//     same one), and every load instruction reads 64 contiguous bytes of each
-//     of the 16 rows.
-//   * Q: the A operand has 16 rows; row m holds query head kvh*g + m % g, so
-//     the g heads are replicated and every lane receives the scores of all g
-//     heads for its own token (g = 1, 2, 4).
-//   * K/V rows of NBUF groups are loaded together (one register buffer per
-//     group) and then computed in order.
-//   * Softmax: each lane keeps its own running max / sum per head, base 2
-//     with scale * log2(e) folded in, and rescales lazily: only when some
-//     lane's score exceeds its max by more than kTau, so p <= 2^kTau.  The
-//     function is unchanged; only the reference point of the exponentials
-//     moves.
-//   * PV: V rows arrive in the same layout; each lane accumulates p * v for
-//     its token into o[g][D/4] in fp32 (VALU FMAs).
-//   * End of split: the 16 token lanes holding the same dims are merged
-//     with DPP butterflies.  A request with one split writes bf16 output
-//     directly; otherwise the split writes (m, l, un-normalised o) to the
-//     workspace.
+//   * S^T = K Q^T on MFMA 16x16x32 bf16: each lane's K loads (8 dims of its
+//     token's row per 32-dim block) are the A operand as loaded; the g query
+//     heads sharing the KV head are replicated over the 16 B columns.
+//   * Softmax: base 2 with scale * log2(e) folded in, lazy rescaling (only
+//     when a score exceeds the running max by more than kTau, so p <= 2^kTau;
+//     the function is unchanged, only the reference point moves).
+//   * O += P V on MFMA 16x16x32 per pair of groups: P straight from the S^T
+//     registers (bf16), V staged row-major in LDS and read key-contiguous
+//     with ds_read_b64_tr_b16.
+//   * K/V rows of a chunk of groups are loaded together, then computed.
+//   * A request with one split writes bf16 output directly; otherwise the
+//     split writes (m, l, un-normalised o) to the workspace.
 // decode_combine_kernel -- one wavefront per (r, query head) with >= 2
 //   splits merges the partials (flash-decoding): M = max m_s,
 //   L = sum l_s 2^(m_s-M), out = sum o_s 2^(m_s-M) / L.
