@@ -122,7 +122,8 @@ def _replicate(w, R):
     return reps
 
 
-def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0):
+def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
+                  fused_store: bool = True):
     import torch
 
     import paged_kv_attention_out_amd as pkv
@@ -151,7 +152,15 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0):
             st = (c.k_new.data_ptr(), c.v_new.data_ptr(), c.out_loc.data_ptr(),
                   c.k_new.shape[0], c.k_cache.data_ptr(), c.v_cache.data_ptr(),
                   c.k_cache.shape[0] * ps, Hkv, d, stream)
-        if is_decode:
+        if is_decode and st is not None and fused_store:
+            # one call: the new rows are written to the pool by the decode kernel
+            at = (c.q.data_ptr(), c.k_new.data_ptr(), c.v_new.data_ptr(), c.out_loc.data_ptr(),
+                  c.k_cache.data_ptr(), c.v_cache.data_ptr(), ps, c.num_pages,
+                  c.page_table.data_ptr(), c.page_table.shape[1], c.seq_lens.data_ptr(), B,
+                  w.max_seq_len, Hq, Hkv, d, w.scale, split_tokens, out.data_ptr(), ws_ptr,
+                  ws_bytes, stream)
+            st = None
+        elif is_decode:
             at = (c.q.data_ptr(), c.k_cache.data_ptr(), c.v_cache.data_ptr(), ps, c.num_pages,
                   c.page_table.data_ptr(), c.page_table.shape[1], c.seq_lens.data_ptr(), B,
                   w.max_seq_len, Hq, Hkv, d, w.scale, split_tokens, out.data_ptr(), ws_ptr,
@@ -164,7 +173,9 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0):
                   stream)
         calls.append((st, at, out))
     f_store = lib.pkv_store_kv
-    f_attn = lib.pkv_paged_attn_decode if is_decode else lib.pkv_paged_attn_prefill
+    fused = is_decode and w.k_new is not None and fused_store
+    f_attn = (lib.pkv_decode_step if fused else
+              lib.pkv_paged_attn_decode if is_decode else lib.pkv_paged_attn_prefill)
 
     def step(i, ev=None):
         st, at, _ = calls[i % R]
@@ -180,24 +191,115 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # Whole-step throughput: K steps between two synchronisations, nothing
+    # else enqueued.
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    # Per-call GPU time: a second pass with HIP events around each attention
+    # call on the launch stream.
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         step(i, events[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     kernel_ms = [a.elapsed_time(b) for a, b in events]
     for _, _, out in calls:
         if not torch.isfinite(out.float()).all():
             raise RuntimeError(f"{name}: non-finite output")
     if R > 1 and not torch.equal(calls[0][2], calls[1][2]):
         raise RuntimeError(f"{name}: replicas disagree")
-    res = dict(workload=w, replicas=R, split=split, ms_per_step=(t1 - t0) * 1e3 / steps,
+    res = dict(workload=w, replicas=R, split=split, fused=fused,
+               ms_per_step=(t1 - t0) * 1e3 / steps,
                kernel_ms_mean=float(np.mean(kernel_ms)), kernel_ms_median=float(np.median(kernel_ms)),
                kernel_ms_min=float(np.min(kernel_ms)))
     return res
+
+
+def time_store(name: str, steps: int, warmup: int):
+    """store_kv alone on a workload's new rows (events around each call)."""
+    import torch
+
+    import paged_kv_attention_out_amd as pkv
+    from paged_kv_attention_out_amd import inputs
+
+    lib = pkv.lib()
+    w = inputs.make_workload(name, device="cuda", poison=False)
+    T = w.k_new.shape[0]
+    nbytes = store_bytes(w)
+    R = max(1, min(64, math.ceil(MIN_WORKING_SET / max(nbytes, 1))))
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = []
+    for _ in range(R):   # distinct source rows per replica; the pool is shared
+        kn, vn = w.k_new.clone(), w.v_new.clone()
+        calls.append((kn, vn, (kn.data_ptr(), vn.data_ptr(), w.out_loc.data_ptr(), T,
+                               w.k_cache.data_ptr(), w.v_cache.data_ptr(),
+                               w.k_cache.shape[0] * w.page_size, w.num_kv_heads, w.head_dim,
+                               stream)))
+    f = lib.pkv_store_kv
+    for i in range(warmup):
+        f(*calls[i % R][2])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        if f(*calls[i % R][2]) != 0:
+            raise RuntimeError("pkv_store_kv failed")
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return {"rows": T, "us_mean": round(ms * 1e3, 2), "bytes": nbytes,
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def time_graph_step(name: str, steps: int, warmup: int):
+    """The decode step (pkv_decode_step) captured once per pool replica in a
+    HIP graph and replayed."""
+    import torch
+
+    import paged_kv_attention_out_amd as pkv
+    from paged_kv_attention_out_amd import inputs
+
+    w = inputs.make_workload(name, device="cuda", poison=False)
+    R = max(1, min(64, math.ceil(MIN_WORKING_SET / max(decode_bytes(w), 1))))
+    reps = _replicate(w, R)
+    ws = pkv.decode_workspace(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                              w.max_seq_len)
+    outs = [torch.empty_like(c.q) for c in reps]
+
+    def step(c, out):
+        pkv.pkv_decode_step(c.q, c.k_new, c.v_new, c.out_loc, c.k_cache, c.v_cache,
+                            c.page_table, c.seq_lens, w.max_seq_len, w.scale, out=out,
+                            workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(reps[0], outs[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for c, out in zip(reps, outs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(c, out)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    if not torch.isfinite(outs[0].float()).all():
+        raise RuntimeError("graph replay: non-finite output")
+    return {"ms_per_step": round(ms, 5), "replicas": R,
+            "GB/s": round((decode_bytes(w) + store_bytes(w)) / (ms * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1)}
 
 
 # ---- CPU baseline (the oracle) ------------------------------------------------
@@ -250,6 +352,8 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true")
+    ap.add_argument("--separate-store", action="store_true",
+                    help="time pkv_store_kv + pkv_paged_attn_decode instead of pkv_decode_step")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (a known "
@@ -278,13 +382,16 @@ def main():
     log(f"device: {props.name} CUs={props.multi_processor_count} "
         f"arch={getattr(props, 'gcnArchName', '?')} lib={pkv.version()}")
 
-    r = time_workload(args.workload, args.steps, args.warmup, args.split_tokens)
+    r = time_workload(args.workload, args.steps, args.warmup, args.split_tokens,
+                      fused_store=not args.separate_store)
     w = r["workload"]
     if w.kind != "decode":
         raise SystemExit("the primary line is a decode workload")
     step_bytes = decode_bytes(w) + store_bytes(w)
     value = step_bytes / (r["ms_per_step"] * 1e-3) / 1e9
-    achieved = decode_bytes(w) / (r["kernel_ms_mean"] * 1e-3) / 1e9
+    # bytes of the timed call: with the fused step it also moves the new rows
+    call_bytes = step_bytes if r["fused"] else decode_bytes(w)
+    achieved = call_bytes / (r["kernel_ms_mean"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -303,14 +410,18 @@ def main():
                    "head_dim": w.head_dim, "page_size": w.page_size,
                    "seq_lens_sum": int(w.seq_lens_np.sum()), "seed": w.seed,
                    "replicas": r["replicas"], "split_tokens": r["split"],
-                   "step": "store_kv + paged decode", "parallelism": "single GPU"},
+                   "step": ("pkv_decode_step (store_kv fused into paged decode)" if r["fused"]
+                            else "pkv_store_kv + pkv_paged_attn_decode"),
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload),
-                     "kernel": "decode call (decode_split_kernel + decode_combine_kernel)",
+                     "kernel": ("decode step call (decode_split_kernel with the fused store + "
+                                "decode_combine_kernel)" if r["fused"] else
+                                "decode call (decode_split_kernel + decode_combine_kernel)"),
                      "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 2),
                      "kernel_us_median": round(r["kernel_ms_median"] * 1e3, 2),
-                     "bytes_per_launch": decode_bytes(w)},
+                     "bytes_per_launch": call_bytes},
     }
     if not args.no_also:
         also = {}
@@ -334,6 +445,10 @@ def main():
                               "tokens_per_s": round(wa.num_tokens / (a["ms_per_step"] * 1e-3), 1),
                               "flops": prefill_flops(wa), "replicas": a["replicas"]}
             del a, wa
+        also["store_kv"] = {n: time_store(n, max(20, args.steps // 5), 3)
+                            for n in ("llama_decode", "chunked_prefill")}
+        also["llama_decode_graph_step"] = time_graph_step(args.workload, args.steps,
+                                                          args.warmup)
         line["also"] = also
         line["tokens_per_s"] = round(w.num_seqs / (r["ms_per_step"] * 1e-3), 1)
     if not args.no_cpu_baseline:

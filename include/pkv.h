@@ -152,6 +152,44 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_decode_step -- one decode step of the batch in one call: the new
+ * token's K/V rows are written to the pool (as pkv_store_kv) and every
+ * request's query attends to its whole context (as pkv_paged_attn_decode).
+ *
+ * The engine's decode step first writes each sequence's new K/V row to the
+ * slot out_loc assigns it and then runs attention over all tokens so far
+ * (mini-sglang "Engine Class", forward_batch with out_loc; miniVLLM "Engine
+ * Architecture", prepare_decode: slot_mapping of the one new token per
+ * sequence).  Here the attention reads the new token's rows straight from
+ * k_new / v_new while the same kernel writes them to the pool, so the step
+ * is one launch (plus the split merge) instead of two.
+ *
+ * Arguments are those of pkv_paged_attn_decode plus:
+ *   k_new, v_new : [num_seqs, num_kv_heads, head_dim] bf16, the rows of the
+ *                  token at position seq_lens[r] - 1 of request r
+ *   out_loc      : [num_seqs] int32, the slot of that token: it must be the
+ *                  slot the page table gives position seq_lens[r] - 1, and no
+ *                  other request of the call may read it.  Slots outside
+ *                  [0, num_pages * page_size) are not written; a request with
+ *                  seq_lens[r] <= 0 has no new token and its out_loc entry is
+ *                  not used.
+ *   k_cache,
+ *   v_cache      : written at the out_loc slots (caller-owned, as above).
+ *
+ * Result: bit-identical to pkv_store_kv followed by pkv_paged_attn_decode on
+ * the same stream.  Errors as pkv_paged_attn_decode; k_new, v_new or out_loc
+ * NULL (with num_seqs > 0) or k_new / v_new not 16-byte aligned -> PKV_EINVAL.
+ */
+int pkv_decode_step(const void* q, const void* k_new, const void* v_new,
+                    const int32_t* out_loc, void* k_cache, void* v_cache,
+                    int32_t page_size, int64_t num_pages, const int32_t* page_table,
+                    int32_t page_table_stride, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                    int32_t split_tokens, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * pkv_paged_attn_prefill -- causal attention of a flat ragged batch of new
  * tokens over their cached prefix and themselves.
  *

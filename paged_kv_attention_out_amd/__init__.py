@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     decode_workspace,
     lib,
     pkv_decode_split_tokens,
+    pkv_decode_step,
     pkv_decode_workspace_bytes,
     pkv_paged_attn_decode,
     pkv_paged_attn_prefill,

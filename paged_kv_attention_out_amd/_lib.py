@@ -37,6 +37,10 @@ SIGNATURES = {
         _i64, _c_void_p, _i32, _i32, _i32, _i32, _f32, _c_void_p, _c_void_p, _size,
         _c_void_p]),
     "pkv_prefill_workspace_bytes": (_size, []),
+    "pkv_decode_step": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
+        _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p,
+        _c_void_p, _size, _c_void_p]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -153,6 +157,34 @@ def pkv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
         _ptr(q), _ptr(k_cache), _ptr(v_cache), ps, num_pages, _ptr(page_table),
         page_table.shape[1], _ptr(seq_lens), B, max_seq_len, Hq, Hkv, d, softmax_scale,
         split_tokens, _ptr(out), _ptr(workspace), ws_bytes, _stream(q)), "pkv_paged_attn_decode")
+    return out
+
+
+def pkv_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    out_loc: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                    softmax_scale: float, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    split_tokens: int = 0) -> torch.Tensor:
+    """Store the new token's K/V rows and run decode attention in one call."""
+    for t, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                    (v_cache, "v_cache")):
+        _dev(t, torch.bfloat16, name)
+    for t, name in ((out_loc, "out_loc"), (page_table, "page_table"), (seq_lens, "seq_lens")):
+        _dev(t, torch.int32, name)
+    B, Hq, d = q.shape
+    num_pages, ps, Hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out")
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, Hkv, d, max_seq_len, split_tokens, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_decode_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out_loc), _ptr(k_cache), _ptr(v_cache), ps,
+        num_pages, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, max_seq_len, Hq,
+        Hkv, d, softmax_scale, split_tokens, _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
+        "pkv_decode_step")
     return out
 
 

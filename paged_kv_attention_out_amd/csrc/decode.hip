@@ -47,6 +47,15 @@ struct DecodeParams {
   const int32_t* page_table;
   const int32_t* seq_lens;
   uint16_t* out;
+  // Fused step (pkv_decode_step): the new token of request r (position
+  // seq_lens[r] - 1, slot out_loc[r]) is read from k_new/v_new [B, Hkv, d]
+  // and written to the pools; null for a plain decode call.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* out_loc;
+  uint16_t* k_pool;  // the pools, writable (same memory as k_cache / v_cache)
+  uint16_t* v_pool;
+  int64_t num_slots;
   float* ws_m;  // [B * Hkv * n_split_max * g]
   float* ws_l;
   float* ws_o;  // [B * Hkv * n_split_max * g * D]
@@ -216,6 +225,18 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   const int t_end = min(n, t_begin + p.split);
 
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
+  // Fused step: the request's last split writes this head's slice of the
+  // new token's K/V rows to slot out_loc[r] (out-of-range slots are
+  // skipped).  No wave of this call reads that slot from the pool.
+  if (p.k_new != nullptr && split == ns - 1 && lane < D / 8) {
+    const int64_t slot = p.out_loc[r];
+    if (slot >= 0 && slot < p.num_slots) {
+      const int64_t src = ((int64_t)r * p.num_kv_heads + kvh) * D + 8 * lane;
+      const int64_t dst = slot * row_elems + (int64_t)kvh * D + 8 * lane;
+      *reinterpret_cast<uint4*>(p.k_pool + dst) = ld16(p.k_new + src);
+      *reinterpret_cast<uint4*>(p.v_pool + dst) = ld16(p.v_new + src);
+    }
+  }
   const int64_t page_elems = row_elems << p.page_shift;
   const int lane_off = (j * p.num_kv_heads + kvh) * D + 8 * c;
 
@@ -225,11 +246,17 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
     return (int64_t)page * page_elems + (int64_t)(t0 & (p.page_size - 1)) * row_elems;
   };
 
+  // Fused step: the lane whose token is the new one (position n - 1) reads
+  // its row from k_new / v_new instead of the pool.
+  const int t_new = p.k_new != nullptr ? n - 1 : -1;
+  const int64_t new_off = ((int64_t)r * p.num_kv_heads + kvh) * D + 8 * c;
+
   uint4 kb[NBUF][KCH], vb[NBUF][KCH];
-  auto load_group = [&](int t0, int loff, int buf) {
+  auto load_group = [&](int t0, int loff, int row, int buf) {
     const int64_t goff = group_offset(t0) + loff;
-    const uint16_t* kp = p.k_cache + goff;
-    const uint16_t* vp = p.v_cache + goff;
+    const bool fresh = t0 + row == t_new;
+    const uint16_t* kp = fresh ? p.k_new + new_off : p.k_cache + goff;
+    const uint16_t* vp = fresh ? p.v_new + new_off : p.v_cache + goff;
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
       if (b == buf) {
@@ -364,7 +391,7 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
     int g = 0;
     for (; g + NBUF <= nfull; g += NBUF) {
 #pragma unroll
-      for (int b = 0; b < NBUF; ++b) load_group(w0 + 16 * (g + b), lane_off, b);
+      for (int b = 0; b < NBUF; ++b) load_group(w0 + 16 * (g + b), lane_off, j, b);
       __builtin_amdgcn_sched_barrier(0);  // every load of the chunk issues first
 #pragma unroll
       for (int b = 0; b < NBUF; b += 2) {
@@ -381,11 +408,11 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
       const int va = g < nfull ? 16 : tail;
       const int vbv = g + 1 < nfull ? 16 : (g + 1 == nfull ? tail : 0);
       const int ja = j < va ? j : va - 1;  // rows past the end repeat the last valid row
-      load_group(w0 + 16 * g, (ja * p.num_kv_heads + kvh) * D + 8 * c, 0);
+      load_group(w0 + 16 * g, (ja * p.num_kv_heads + kvh) * D + 8 * c, ja, 0);
       f32x4 sb = {0.f, 0.f, 0.f, 0.f};
       if (vbv > 0) {
         const int jb = j < vbv ? j : vbv - 1;
-        load_group(w0 + 16 * (g + 1), (jb * p.num_kv_heads + kvh) * D + 8 * c, 1);
+        load_group(w0 + 16 * (g + 1), (jb * p.num_kv_heads + kvh) * D + 8 * c, jb, 1);
         sb = scores(1);
         stage_v(1, 1);
       } else {
@@ -591,14 +618,14 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
       .total;
 }
 
-extern "C" int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                                     int32_t page_size, int64_t num_pages,
-                                     const int32_t* page_table, int32_t page_table_stride,
-                                     const int32_t* seq_lens, int32_t num_seqs,
-                                     int32_t max_seq_len, int32_t num_q_heads,
-                                     int32_t num_kv_heads, int32_t head_dim,
-                                     float softmax_scale, int32_t split_tokens, void* out,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int decode_impl(const void* q, const void* k_new, const void* v_new, const int32_t* out_loc,
+                const void* k_cache, const void* v_cache, int32_t page_size, int64_t num_pages,
+                const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
+                int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                int32_t head_dim, float softmax_scale, int32_t split_tokens, void* out,
+                void* workspace, size_t workspace_bytes, void* stream) {
   using namespace pkv_host;
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                        split_tokens))
@@ -607,6 +634,9 @@ extern "C" int pkv_paged_attn_decode(const void* q, const void* k_cache, const v
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out) return PKV_EINVAL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return PKV_EINVAL;
+  const bool fused = k_new != nullptr || v_new != nullptr || out_loc != nullptr;
+  if (fused && (!k_new || !v_new || !out_loc || !aligned16(k_new) || !aligned16(v_new)))
     return PKV_EINVAL;
   if (num_pages <= 0 || page_table_stride <= 0) return PKV_EINVAL;
   if (!is_pow2_page(page_size)) return PKV_EUNSUPPORTED;
@@ -628,12 +658,9 @@ extern "C" int pkv_paged_attn_decode(const void* q, const void* k_cache, const v
     p.ws_l = reinterpret_cast<float*>(ws + w.l);
     p.ws_o = reinterpret_cast<float*>(ws + w.o);
   }
-  const int64_t units = rk * nsm;
-  // One wave per block: blocks go round-robin to the 8 XCDs, so with the KV
-  // head as the fastest unit index each XCD takes the same heads of every
-  // (request, split) -- equal work per XCD whatever the lengths -- while the
-  // heads sharing a page are dispatched together.
-  const int64_t blocks = units;
+  // One block per (request, split) pair and KV head, at most units blocks;
+  // blocks past the pairs that exist exit at once.
+  const int64_t blocks = rk * nsm;
   if (blocks > INT32_MAX) return PKV_EINVAL;
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -641,6 +668,14 @@ extern "C" int pkv_paged_attn_decode(const void* q, const void* k_cache, const v
   p.page_table = page_table;
   p.seq_lens = seq_lens;
   p.out = static_cast<uint16_t*>(out);
+  if (fused) {
+    p.k_new = static_cast<const uint16_t*>(k_new);
+    p.v_new = static_cast<const uint16_t*>(v_new);
+    p.out_loc = out_loc;
+    p.k_pool = const_cast<uint16_t*>(p.k_cache);
+    p.v_pool = const_cast<uint16_t*>(p.v_cache);
+    p.num_slots = num_pages * page_size;
+  }
   p.num_pages = num_pages;
   p.page_size = page_size;
   p.page_shift = log2_exact(page_size);
@@ -661,4 +696,35 @@ extern "C" int pkv_paged_attn_decode(const void* q, const void* k_cache, const v
   if (g == 1) return launch_decode<128, 1>(p, blocks, s);
   if (g == 2) return launch_decode<128, 2>(p, blocks, s);
   return launch_decode<128, 4>(p, blocks, s);
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                     int32_t page_size, int64_t num_pages,
+                                     const int32_t* page_table, int32_t page_table_stride,
+                                     const int32_t* seq_lens, int32_t num_seqs,
+                                     int32_t max_seq_len, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim,
+                                     float softmax_scale, int32_t split_tokens, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, nullptr, nullptr, nullptr, k_cache, v_cache, page_size, num_pages,
+                     page_table, page_table_stride, seq_lens, num_seqs, max_seq_len,
+                     num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
+                     workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_decode_step(const void* q, const void* k_new, const void* v_new,
+                               const int32_t* out_loc, void* k_cache, void* v_cache,
+                               int32_t page_size, int64_t num_pages, const int32_t* page_table,
+                               int32_t page_table_stride, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                               int32_t split_tokens, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new || !out_loc)) return PKV_EINVAL;
+  return decode_impl(q, k_new, v_new, out_loc, k_cache, v_cache, page_size, num_pages,
+                     page_table, page_table_stride, seq_lens, num_seqs, max_seq_len,
+                     num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
+                     workspace, workspace_bytes, stream);
 }

@@ -95,6 +95,26 @@ def test_decode_validation(kw, status):
     assert _decode(**kw) == status
 
 
+def _step(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, loc=FAKE, kc=FAKE, vc=FAKE, ps=16, pages=100, pt=FAKE,
+             stride=128, seq=FAKE, B=4, maxlen=2048, hq=32, hkv=8, d=64, scale=0.125, split=0,
+             out=FAKE, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_decode_step(
+        a["q"], a["kn"], a["vn"], a["loc"], a["kc"], a["vc"], a["ps"], a["pages"], a["pt"],
+        a["stride"], a["seq"], a["B"], a["maxlen"], a["hq"], a["hkv"], a["d"], a["scale"],
+        a["split"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), 1), (dict(vn=None), 1), (dict(loc=None), 1), (dict(kn=FAKE + 8), 1),
+    (dict(vn=FAKE + 2), 1), (dict(q=None), 1), (dict(d=96), 2), (dict(hq=64), 2),
+    (dict(wsb=100, ws=FAKE), 3), (dict(B=0, kn=None, vn=None, loc=None), 0),
+])
+def test_decode_step_validation(kw, status):
+    assert _step(**kw) == status
+
+
 def test_decode_workspace_sizes():
     # one split per request: no workspace
     assert pkv.pkv_decode_workspace_bytes(1, 4, 2, 64, 64) == 0

@@ -171,3 +171,53 @@ def test_decode_workspace_reuse_across_shapes():
         out = run_decode(w, split_tokens=64, workspace=ws)
         torch.cuda.synchronize()
         assert_close(f64(out), _oracle(w), "reuse")
+
+
+STEP_CASES = [
+    (4, 32, 8, 64, 16, [1, 17, 300, 2048], 0),      # one-token request; new token in a full chunk
+    (3, 16, 8, 128, 256, [256, 513, 4000], 0),
+    (5, 8, 2, 64, 32, [16, 48, 95, 1000, 64], 64),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: f"B{c[0]}-hq{c[1]}-hkv{c[2]}-d{c[3]}-ps{c[4]}")
+def test_decode_step_equals_store_then_decode(case):
+    """pkv_decode_step (one launch) against pkv_store_kv + pkv_paged_attn_decode:
+    bit-identical output and pools, and within tolerance of the oracle."""
+    B, hq, hkv, d, ps, lens, split = case
+    print(f"decode step case {case}", flush=True)
+    w = inputs.build_decode(B, hq, hkv, d, ps, lens, seed=77 + d + B, device="cuda",
+                            store_new=True)
+    ref = _oracle(w)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    run_store(w)
+    out_a = run_decode(w, split_tokens=split).clone()
+    ka, va = w.k_cache.clone(), w.v_cache.clone()
+    w.k_cache.copy_(k0)
+    w.v_cache.copy_(v0)
+    out_b = pkv.pkv_decode_step(w.q, w.k_new, w.v_new, w.out_loc, w.k_cache, w.v_cache,
+                                w.page_table, w.seq_lens, w.max_seq_len, w.scale,
+                                split_tokens=split)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    assert torch.equal(ka.view(torch.int16), w.k_cache.view(torch.int16))
+    assert torch.equal(va.view(torch.int16), w.v_cache.view(torch.int16))
+    assert_close(f64(out_b), ref, "decode step")
+
+
+def test_decode_step_llama_workload():
+    w = inputs.make_workload("llama_decode", device="cuda")
+    reqs = [0, 7, 33, 63]
+    kc, vc = host_pools(w)
+    ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale,
+                     requests=reqs)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    run_store(w)
+    out_a = run_decode(w).clone()
+    w.k_cache.copy_(k0)
+    w.v_cache.copy_(v0)
+    out_b = pkv.pkv_decode_step(w.q, w.k_new, w.v_new, w.out_loc, w.k_cache, w.v_cache,
+                                w.page_table, w.seq_lens, w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    print("llama decode step max/mean err", assert_close(f64(out_b), ref, "llama step"))
