@@ -302,6 +302,48 @@ def time_graph_step(name: str, steps: int, warmup: int):
             "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1)}
 
 
+def time_metadata(steps: int):
+    """The device-side metadata builders on the chunked-prefill and
+    Llama-decode batches (events around each call)."""
+    import torch
+
+    import paged_kv_attention_out_amd as pkv
+    from paged_kv_attention_out_amd import inputs
+
+    res = {}
+    wp = inputs.make_workload("chunked_prefill", device="cuda", poison=False)
+    wd = inputs.make_workload("llama_decode", device="cuda", poison=False)
+    cu = torch.empty_like(wp.cu_seqlens_q)
+    loc_p = torch.empty_like(wp.out_loc)
+    loc_d = torch.empty_like(wd.out_loc)
+    calls = {
+        "prefill_metadata": lambda: pkv.pkv_prefill_metadata(
+            wp.seq_lens, wp.prefix_lens, wp.page_table, wp.page_size, wp.num_tokens,
+            cu_seqlens_q=cu, out_loc=loc_p),
+        "decode_metadata": lambda: pkv.pkv_decode_metadata(wd.seq_lens, wd.page_table,
+                                                           wd.page_size, out_loc=loc_d),
+    }
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        res[name] = {"us_mean": round(float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3,
+                                      2)}
+    res["prefill_metadata"]["tokens"] = wp.num_tokens
+    res["decode_metadata"]["requests"] = wd.num_seqs
+    if not (torch.equal(cu, wp.cu_seqlens_q) and torch.equal(loc_p, wp.out_loc)
+            and torch.equal(loc_d, wd.out_loc)):
+        raise RuntimeError("metadata builders disagree with the workloads")
+    return res
+
+
 # ---- CPU baseline (the oracle) ------------------------------------------------
 
 def cpu_baseline(name: str, budget_s: float):
@@ -449,6 +491,7 @@ def main():
                             for n in ("llama_decode", "chunked_prefill")}
         also["llama_decode_graph_step"] = time_graph_step(args.workload, args.steps,
                                                           args.warmup)
+        also["metadata"] = time_metadata(max(20, args.steps // 5))
         line["also"] = also
         line["tokens_per_s"] = round(w.num_seqs / (r["ms_per_step"] * 1e-3), 1)
     if not args.no_cpu_baseline:

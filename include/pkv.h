@@ -245,6 +245,54 @@ int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q,
 /* Bytes of workspace pkv_paged_attn_prefill needs (a small constant). */
 size_t pkv_prefill_workspace_bytes(void);
 
+/*
+ * pkv_prefill_metadata -- build a prefill batch's cu_seqlens_q and
+ * slot_mapping (out_loc) on the device from lengths and the page table.
+ *
+ * The prefill batch holds only the tokens after each sequence's cached
+ * prefix; cu_seqlens_q accumulates their counts, e.g. [0, 5, 8, 12], and
+ * slot_mapping gives every new token the cache slot it is written to
+ * (miniVLLM "Engine Architecture", ModelRunner / prepare_prefill).  New token
+ * i of request r is at position prefix_lens[r] + i; its slot is
+ * page_table[r, t / page_size] * page_size + t % page_size with that t.
+ *
+ *   seq_lens     : [num_seqs] int32, tokens of each sequence including the
+ *                  new ones
+ *   prefix_lens  : [num_seqs] int32, cached tokens (the new count is
+ *                  max(seq_lens[r] - max(prefix_lens[r], 0), 0))
+ *   page_table   : [num_seqs, page_table_stride] int32
+ *   page_size    : > 0 (any value)
+ *   max_tokens   : capacity of out_loc; tokens at flat index >= max_tokens
+ *                  are not written
+ *   cu_seqlens_q : [num_seqs + 1] int32, written
+ *   out_loc      : [max_tokens] int32, written for flat indices below the
+ *                  total; a position outside the page-table row gets -1
+ *                  (pkv_store_kv skips it)
+ *
+ * Host-checkable errors: null pointers, num_seqs < 0, max_tokens < 0,
+ * page_table_stride <= 0 or page_size <= 0 -> PKV_EINVAL.  num_seqs == 0 is
+ * a no-op.
+ */
+int pkv_prefill_metadata(const int32_t* seq_lens, const int32_t* prefix_lens,
+                         int32_t num_seqs, const int32_t* page_table,
+                         int32_t page_table_stride, int32_t page_size,
+                         int32_t max_tokens, int32_t* cu_seqlens_q,
+                         int32_t* out_loc, void* stream);
+
+/*
+ * pkv_decode_metadata -- the decode step's slot_mapping on the device: each
+ * sequence contributes its most recent token, at position seq_lens[r] - 1
+ * (context_lens counts every token so far), and out_loc[r] is that token's
+ * slot (miniVLLM "Engine Architecture", prepare_decode).  A sequence with
+ * seq_lens[r] <= 0 (a padding row) or whose position falls outside its
+ * page-table row gets -1.
+ *
+ * Errors as pkv_prefill_metadata.
+ */
+int pkv_decode_metadata(const int32_t* seq_lens, int32_t num_seqs,
+                        const int32_t* page_table, int32_t page_table_stride,
+                        int32_t page_size, int32_t* out_loc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

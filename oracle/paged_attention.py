@@ -79,6 +79,39 @@ def request_slots(page_table_row: np.ndarray, n: int, page_size: int) -> np.ndar
     return pages * page_size + pos % page_size
 
 
+def slot_of(page_table_row: np.ndarray, t: int, page_size: int) -> int:
+    """Flat slot of logical position t, or -1 when t lies outside the row
+    (the same page / row rule as ``request_slots``)."""
+    i = t // page_size
+    if t < 0 or i >= len(page_table_row):
+        return -1
+    return int(page_table_row[i]) * page_size + t % page_size
+
+
+def prefill_metadata(seq_lens, prefix_lens, page_table: np.ndarray, page_size: int):
+    """cu_seqlens_q and slot_mapping of a prefill batch (miniVLLM "Engine
+    Architecture", prepare_prefill): only the tokens after each sequence's
+    cached prefix are fed, ``cu_seqlens_q`` accumulates their counts
+    (``len(seq) - num_cached_tokens``), and each new token gets the slot of
+    its position."""
+    cu, slots = [0], []
+    for r, (n, c) in enumerate(zip(seq_lens, prefix_lens)):
+        first = max(int(c), 0)
+        count = max(int(n) - first, 0)
+        cu.append(cu[-1] + count)
+        for i in range(count):
+            slots.append(slot_of(page_table[r], first + i, page_size))
+    return np.array(cu, dtype=np.int32), np.array(slots, dtype=np.int32)
+
+
+def decode_slots(seq_lens, page_table: np.ndarray, page_size: int) -> np.ndarray:
+    """slot_mapping of a decode step (miniVLLM prepare_decode): each sequence
+    contributes its most recent token, at position context_len - 1; a padding
+    row (length <= 0) gets -1."""
+    return np.array([slot_of(page_table[r], int(n) - 1, page_size) if int(n) > 0 else -1
+                     for r, n in enumerate(seq_lens)], dtype=np.int32)
+
+
 def gather(cache: np.ndarray, page_table_row: np.ndarray, n: int) -> np.ndarray:
     """Contiguous ``[n, Hkv, d]`` float64 copy of one request's K or V."""
     ps = cache.shape[1]

@@ -37,6 +37,10 @@ SIGNATURES = {
         _i64, _c_void_p, _i32, _i32, _i32, _i32, _f32, _c_void_p, _c_void_p, _size,
         _c_void_p]),
     "pkv_prefill_workspace_bytes": (_size, []),
+    "pkv_prefill_metadata": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _c_void_p, _i32, _i32,
+                                             _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "pkv_decode_metadata": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _i32, _i32, _c_void_p,
+                                            _c_void_p]),
     "pkv_decode_step": (ctypes.c_int, [
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
         _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p,
@@ -186,6 +190,43 @@ def pkv_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         Hkv, d, softmax_scale, split_tokens, _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
         "pkv_decode_step")
     return out
+
+
+def pkv_prefill_metadata(seq_lens: torch.Tensor, prefix_lens: torch.Tensor,
+                         page_table: torch.Tensor, page_size: int, max_tokens: int,
+                         cu_seqlens_q: Optional[torch.Tensor] = None,
+                         out_loc: Optional[torch.Tensor] = None):
+    """cu_seqlens_q ``[B+1]`` and out_loc ``[max_tokens]`` of a prefill batch."""
+    for t, name in ((seq_lens, "seq_lens"), (prefix_lens, "prefix_lens"),
+                    (page_table, "page_table")):
+        _dev(t, torch.int32, name)
+    B = seq_lens.numel()
+    if cu_seqlens_q is None:
+        cu_seqlens_q = torch.empty(B + 1, dtype=torch.int32, device=seq_lens.device)
+    if out_loc is None:
+        out_loc = torch.empty(max(max_tokens, 1), dtype=torch.int32, device=seq_lens.device)
+    _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q")
+    _dev(out_loc, torch.int32, "out_loc")
+    _check(lib().pkv_prefill_metadata(
+        _ptr(seq_lens), _ptr(prefix_lens), B, _ptr(page_table), page_table.shape[1], page_size,
+        max_tokens, _ptr(cu_seqlens_q), _ptr(out_loc), _stream(seq_lens)),
+        "pkv_prefill_metadata")
+    return cu_seqlens_q, out_loc
+
+
+def pkv_decode_metadata(seq_lens: torch.Tensor, page_table: torch.Tensor, page_size: int,
+                        out_loc: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out_loc ``[B]``: the slot of each sequence's newest token."""
+    _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(page_table, torch.int32, "page_table")
+    B = seq_lens.numel()
+    if out_loc is None:
+        out_loc = torch.empty(max(B, 1), dtype=torch.int32, device=seq_lens.device)
+    _dev(out_loc, torch.int32, "out_loc")
+    _check(lib().pkv_decode_metadata(_ptr(seq_lens), B, _ptr(page_table), page_table.shape[1],
+                                     page_size, _ptr(out_loc), _stream(seq_lens)),
+           "pkv_decode_metadata")
+    return out_loc
 
 
 def pkv_prefill_workspace_bytes() -> int:

@@ -1,0 +1,143 @@
+// Device-side step metadata: the per-step arrays the engine otherwise builds
+// on the host and copies over before every forward pass.
+//
+// * Prefill (miniVLLM "Engine Architecture", ModelRunner / prepare_prefill):
+//   the batch holds only the tokens after each sequence's cached prefix;
+//   cu_seqlens_q are the cumulative counts of those new tokens (the pages'
+//   example: [0, 5, 8, 12]), and slot_mapping gives each new token the
+//   physical cache slot it is written to.
+// * Decode (prepare_decode): each sequence contributes one token, its most
+//   recent; context_lens counts every token so far, so the new token sits at
+//   position context_len - 1 and slot_mapping holds that one slot.
+//
+// A token at logical position t of request r lives in physical page
+// page_table[r, t / page_size] at row t % page_size: slot = page *
+// page_size + t % page_size (mini-sglang "Engine Class", Key Attributes:
+// page_table; miniVLLM allocate_kv_cache for the pool layout).
+
+#include "pkv_common.h"
+
+namespace {
+
+struct PrefillMetaParams {
+  const int32_t* seq_lens;
+  const int32_t* prefix_lens;
+  const int32_t* page_table;
+  int32_t* cu_seqlens;
+  int32_t* out_loc;
+  int32_t num_seqs;
+  int32_t pt_stride;
+  int32_t page_size;
+  int32_t max_tokens;
+};
+
+struct DecodeMetaParams {
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int32_t* out_loc;
+  int32_t num_seqs;
+  int32_t pt_stride;
+  int32_t page_size;
+};
+
+// New tokens of request r: seq_len - cached prefix, never negative.
+__device__ __forceinline__ int new_tokens(const PrefillMetaParams& p, int r) {
+  const int n = p.seq_lens[r];
+  const int c = max(p.prefix_lens[r], 0);
+  return max(n - c, 0);
+}
+
+// Slot of logical position t of a request, or -1 when the position falls
+// outside the page-table row.  Only page ids are read; the pool is not.
+__device__ __forceinline__ int32_t slot_of(const int32_t* row, int pt_stride, int page_size,
+                                           int t) {
+  const int i = t / page_size;
+  if (t < 0 || i >= pt_stride) return -1;
+  const int64_t s = (int64_t)row[i] * page_size + t % page_size;
+  return (s < 0 || s > INT32_MAX) ? -1 : (int32_t)s;
+}
+
+// One 256-thread block per request: the block sums the new-token counts of
+// the requests before it (its offset in the flat batch), then writes the
+// slots of its own new tokens.
+__global__ __launch_bounds__(256) void prefill_meta_kernel(PrefillMetaParams p) {
+  __shared__ int part[256];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  int acc = 0;
+  for (int j = tid; j < r; j += 256) acc += new_tokens(p, j);
+  part[tid] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) part[tid] += part[tid + off];
+    __syncthreads();
+  }
+  const int start = part[0];
+  const int len = new_tokens(p, r);
+  if (tid == 0) {
+    if (r == 0) p.cu_seqlens[0] = 0;
+    p.cu_seqlens[r + 1] = start + len;
+  }
+  const int32_t* row = p.page_table + (int64_t)r * p.pt_stride;
+  const int first = max(p.prefix_lens[r], 0);
+  for (int i = tid; i < len; i += 256) {
+    const int t = start + i;
+    if (t >= p.max_tokens) break;
+    p.out_loc[t] = slot_of(row, p.pt_stride, p.page_size, first + i);
+  }
+}
+
+__global__ __launch_bounds__(256) void decode_meta_kernel(DecodeMetaParams p) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= p.num_seqs) return;
+  const int n = p.seq_lens[r];
+  p.out_loc[r] = n <= 0 ? -1
+                        : slot_of(p.page_table + (int64_t)r * p.pt_stride, p.pt_stride,
+                                  p.page_size, n - 1);
+}
+
+}  // namespace
+
+extern "C" int pkv_prefill_metadata(const int32_t* seq_lens, const int32_t* prefix_lens,
+                                    int32_t num_seqs, const int32_t* page_table,
+                                    int32_t page_table_stride, int32_t page_size,
+                                    int32_t max_tokens, int32_t* cu_seqlens_q,
+                                    int32_t* out_loc, void* stream) {
+  using namespace pkv_host;
+  if (num_seqs < 0 || max_tokens < 0) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!seq_lens || !prefix_lens || !page_table || !cu_seqlens_q) return PKV_EINVAL;
+  if (max_tokens > 0 && !out_loc) return PKV_EINVAL;
+  if (page_table_stride <= 0 || page_size <= 0) return PKV_EINVAL;
+  PrefillMetaParams p;
+  p.seq_lens = seq_lens;
+  p.prefix_lens = prefix_lens;
+  p.page_table = page_table;
+  p.cu_seqlens = cu_seqlens_q;
+  p.out_loc = out_loc;
+  p.num_seqs = num_seqs;
+  p.pt_stride = page_table_stride;
+  p.page_size = page_size;
+  p.max_tokens = max_tokens;
+  return launch(prefill_meta_kernel, dim3((unsigned)num_seqs), dim3(256),
+                static_cast<hipStream_t>(stream), p);
+}
+
+extern "C" int pkv_decode_metadata(const int32_t* seq_lens, int32_t num_seqs,
+                                   const int32_t* page_table, int32_t page_table_stride,
+                                   int32_t page_size, int32_t* out_loc, void* stream) {
+  using namespace pkv_host;
+  if (num_seqs < 0) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!seq_lens || !page_table || !out_loc) return PKV_EINVAL;
+  if (page_table_stride <= 0 || page_size <= 0) return PKV_EINVAL;
+  DecodeMetaParams p;
+  p.seq_lens = seq_lens;
+  p.page_table = page_table;
+  p.out_loc = out_loc;
+  p.num_seqs = num_seqs;
+  p.pt_stride = page_table_stride;
+  p.page_size = page_size;
+  return launch(decode_meta_kernel, dim3((unsigned)((num_seqs + 255) / 256)), dim3(256),
+                static_cast<hipStream_t>(stream), p);
+}

@@ -115,6 +115,29 @@ def test_decode_step_validation(kw, status):
     assert _step(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq=None), 1), (dict(pre=None), 1), (dict(pt=None), 1), (dict(cu=None), 1),
+    (dict(loc=None), 1), (dict(B=-1), 1), (dict(maxt=-1), 1), (dict(stride=0), 1),
+    (dict(ps=0), 1), (dict(B=0, seq=None), 0),
+])
+def test_prefill_metadata_validation(kw, status):
+    a = dict(seq=FAKE, pre=FAKE, B=4, pt=FAKE, stride=8, ps=16, maxt=100, cu=FAKE, loc=FAKE)
+    a.update(kw)
+    assert pkv.lib().pkv_prefill_metadata(a["seq"], a["pre"], a["B"], a["pt"], a["stride"],
+                                          a["ps"], a["maxt"], a["cu"], a["loc"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq=None), 1), (dict(pt=None), 1), (dict(loc=None), 1), (dict(B=-1), 1),
+    (dict(stride=0), 1), (dict(ps=-16), 1), (dict(B=0, seq=None), 0),
+])
+def test_decode_metadata_validation(kw, status):
+    a = dict(seq=FAKE, B=4, pt=FAKE, stride=8, ps=16, loc=FAKE)
+    a.update(kw)
+    assert pkv.lib().pkv_decode_metadata(a["seq"], a["B"], a["pt"], a["stride"], a["ps"],
+                                         a["loc"], None) == status
+
+
 def test_decode_workspace_sizes():
     # one split per request: no workspace
     assert pkv.pkv_decode_workspace_bytes(1, 4, 2, 64, 64) == 0

@@ -386,3 +386,42 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         except Exception:  # a failed assertion or a crash both count
             caught.append(pin.__name__)
     assert caught, f"no pin notices the planted mistake {name}"
+
+
+# ---- step metadata (prepare_prefill / prepare_decode) -------------------------
+
+def test_prefill_metadata_golden_cu_seqlens():
+    """The pages' example: three sequences with 5, 3 and 4 new tokens give
+    cu_seqlens_q = [0, 5, 8, 12]."""
+    g = json.load(open(os.path.join(GOLDEN, "cu_seqlens_example.json")))
+    lens = np.array(g["q_lens"], np.int32)
+    table = np.zeros((len(lens), 4), np.int32)
+    cu, slots = orc.prefill_metadata(lens, np.zeros_like(lens), table, 16)
+    assert cu.tolist() == g["cu_seqlens_q"]
+    assert len(slots) == cu[-1]
+
+
+def test_metadata_hand_example():
+    """Page row [7, 2], page size 4: positions 3, 4, 5 sit in page 7 row 3
+    (slot 31), then page 2 rows 0, 1 (slots 8, 9)."""
+    table = np.array([[7, 2], [5, 0]], np.int32)
+    cu, slots = orc.prefill_metadata([6, 2], [3, 0], table, 4)
+    assert cu.tolist() == [0, 3, 5]
+    assert slots.tolist() == [31, 8, 9, 20, 21]
+    assert orc.decode_slots([6, 0], table, 4).tolist() == [9, -1]
+    # a position past the row's pages has no slot
+    assert orc.decode_slots([9], table[:1], 4).tolist() == [-1]
+    # more cached tokens than tokens: nothing new
+    cu, slots = orc.prefill_metadata([3], [5], table[:1], 4)
+    assert cu.tolist() == [0, 0] and len(slots) == 0
+
+
+def test_metadata_matches_the_generators():
+    """The input generators place new tokens with their own slot code; the
+    oracle's metadata must name the same slots."""
+    w = inputs.build_decode(5, 8, 2, 64, 16, [1, 17, 300, 2048, 64], seed=3, store_new=True)
+    assert np.array_equal(orc.decode_slots(w.seq_lens_np, w.page_table_np, 16), w.out_loc_np)
+    w = inputs.build_prefill(3, 8, 2, 64, 32, [0, 40, 33], [70, 1, 200], seed=4)
+    cu, slots = orc.prefill_metadata(w.seq_lens_np, w.prefix_lens_np, w.page_table_np, 32)
+    assert np.array_equal(cu, w.cu_seqlens_q.numpy())
+    assert np.array_equal(slots, w.out_loc_np)
