@@ -57,6 +57,22 @@ def store_bytes(w) -> int:
     return 2 * T * w.num_kv_heads * w.head_dim * 2 * 2 + 4 * T
 
 
+def unique_kv_bytes(w) -> int:
+    """K/V bytes of the distinct pool rows a decode batch reads (pages shared
+    between requests counted once)."""
+    ps = w.page_size
+    rows = set()
+    for r in range(w.num_seqs):
+        n = int(w.seq_lens_np[r])
+        pages = w.page_table_np[r, :(n + ps - 1) // ps]
+        for i, pg in enumerate(pages):
+            rows.add((int(pg), min(ps, n - i * ps)))
+    tokens = {}
+    for pg, cnt in rows:
+        tokens[pg] = max(tokens.get(pg, 0), cnt)
+    return sum(tokens.values()) * w.num_kv_heads * w.head_dim * 2 * 2
+
+
 def prefill_flops(w) -> int:
     L = w.q_lens_np.astype(np.int64)
     P = w.prefix_lens_np.astype(np.int64)
@@ -467,18 +483,25 @@ def main():
     }
     if not args.no_also:
         also = {}
-        for name in ("qwen_decode", "long_decode", "chunked_prefill"):
+        for name in ("qwen_decode", "long_decode", "chunked_prefill", "shared_prefix_decode"):
             torch.cuda.empty_cache()
             steps = max(10, args.steps // 10)
             a = time_workload(name, steps, max(3, args.warmup // 4))
             wa = a["workload"]
             if wa.kind == "decode":
-                gbs = decode_bytes(wa) / (a["kernel_ms_mean"] * 1e-3) / 1e9
+                call_b = decode_bytes(wa) + (store_bytes(wa) if a["fused"] else 0)
+                gbs = call_b / (a["kernel_ms_mean"] * 1e-3) / 1e9
                 also[name] = {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
                               "kernel_us_mean": round(a["kernel_ms_mean"] * 1e3, 2),
                               "ms_per_step": round(a["ms_per_step"], 4),
                               "tokens_per_s": round(wa.num_seqs / (a["ms_per_step"] * 1e-3), 1),
                               "split_tokens": a["split"], "replicas": a["replicas"]}
+                if name == "shared_prefix_decode":
+                    # counting rule: shared pages count once per request; the
+                    # distinct K/V bytes of the batch are far fewer
+                    ub = unique_kv_bytes(wa)
+                    also[name]["unique_kv_bytes"] = ub
+                    also[name]["unique_GB/s"] = round(ub / (a["kernel_ms_mean"] * 1e-3) / 1e9, 1)
             else:
                 tf = prefill_flops(wa) / (a["kernel_ms_mean"] * 1e-3) / 1e12
                 also[name] = {"TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4),

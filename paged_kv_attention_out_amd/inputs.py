@@ -56,6 +56,13 @@ WORKLOADS = {
         kind="decode", num_seqs=16, num_q_heads=16, num_kv_heads=8, head_dim=128,
         page_size=16, len_range=(32768, 131072), store_new=False,
         outlier_frac=0.01, outlier_scale=8.0, seed=1005),
+    # Llama-shaped decode whose requests share a 1024-token cached prefix:
+    # the first 64 pages of every page table alias the same physical pages
+    # (prefix caching), each request then continues with its own pages.
+    "shared_prefix_decode": dict(
+        kind="decode", num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=64,
+        page_size=16, len_range=(1024 + 64, 1024 + 1024), shared_prefix=1024,
+        store_new=True, seed=1006),
 }
 
 POOL_FACTOR = 1.25
@@ -149,10 +156,14 @@ def _generator(seed: int, device) -> torch.Generator:
 
 
 def _assign_pages(rng: np.random.Generator, pages_needed: np.ndarray,
-                  pool_pages: Optional[int], width: int):
-    """Shuffle physical page ids and hand them to requests in order.
+                  pool_pages: Optional[int], width: int, shared: int = 0):
+    """Shuffle physical page ids and hand them to requests in order.  The
+    first ``shared`` pages of every request are the same physical pages
+    (a cached prefix shared by all of them); the rest are private.
     Returns (page_table [B, W], pool size, poison page id)."""
-    total = int(pages_needed.sum())
+    if shared and (pages_needed <= shared).any():
+        raise ValueError("every request needs a private page after the shared prefix")
+    total = int(pages_needed.sum()) - shared * max(len(pages_needed) - 1, 0)
     if pool_pages is None:
         pool_pages = int(math.ceil(POOL_FACTOR * total))
     if pool_pages < total:
@@ -160,10 +171,12 @@ def _assign_pages(rng: np.random.Generator, pages_needed: np.ndarray,
     perm = rng.permutation(pool_pages).astype(np.int32)
     poison = pool_pages
     table = np.full((len(pages_needed), width), poison, dtype=np.int32)
-    off = 0
+    table[:, :shared] = perm[:shared]
+    off = shared
     for r, k in enumerate(pages_needed):
-        table[r, :k] = perm[off:off + k]
-        off += int(k)
+        own = int(k) - shared
+        table[r, shared:shared + own] = perm[off:off + own]
+        off += own
     return table, pool_pages, poison
 
 
@@ -202,7 +215,7 @@ def _poison(cache: torch.Tensor, table: np.ndarray, seq_lens: np.ndarray,
 def build_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                  seq_lens, *, seed, device="cpu", pool_pages=None, width=None,
                  store_new=False, outlier_frac=0.0, outlier_scale=8.0,
-                 poison=True, name="custom_decode") -> Workload:
+                 poison=True, name="custom_decode", shared_pages=0) -> Workload:
     """Decode batch: one query per request at position n_r - 1 attending to
     all n_r tokens.  With ``store_new`` the token at n_r - 1 is not yet in the
     pool: its K/V rows come in ``k_new``/``v_new`` with slots ``out_loc``."""
@@ -213,7 +226,7 @@ def build_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
     need = (seq_lens.astype(np.int64) + ps - 1) // ps
     if width is None:
         width = int(need.max()) if num_seqs else 1
-    table, pool, poison_id = _assign_pages(rng, need, pool_pages, max(width, 1))
+    table, pool, poison_id = _assign_pages(rng, need, pool_pages, max(width, 1), shared_pages)
     gen = _generator(seed, device)
     shape = (pool + 1, ps, num_kv_heads, head_dim)
     k_cache = _randn_bf16(shape, gen, device)
@@ -336,7 +349,7 @@ def make_workload(name: str, *, seed: Optional[int] = None, device="cpu",
             store_new=cfg["store_new"],
             outlier_frac=cfg.get("outlier_frac", 0.0),
             outlier_scale=cfg.get("outlier_scale", 8.0), poison=poison,
-            name=name)
+            name=name, shared_pages=cfg.get("shared_prefix", 0) // ps)
     prefix, qlens = draw_lengths(name, seed)
     width = -(-(cfg["prefix_range"][1] + cfg["new_range"][1]) // ps)
     return build_prefill(

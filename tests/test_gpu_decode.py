@@ -221,3 +221,18 @@ def test_decode_step_llama_workload():
     torch.cuda.synchronize()
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
     print("llama decode step max/mean err", assert_close(f64(out_b), ref, "llama step"))
+
+
+def test_shared_prefix_decode_workload():
+    """Requests whose page tables alias one cached 1024-token prefix
+    (prefix caching): the kernels read the shared pages once per request and
+    per KV head, like any other page."""
+    w = inputs.make_workload("shared_prefix_decode", device="cuda")
+    reqs = [0, 21, 42, 63]
+    kc, vc = host_pools(w)
+    ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale,
+                     requests=reqs)
+    out = pkv.pkv_decode_step(w.q, w.k_new, w.v_new, w.out_loc, w.k_cache, w.v_cache,
+                              w.page_table, w.seq_lens, w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    print("shared prefix max/mean err", assert_close(f64(out), ref, "shared prefix"))

@@ -97,3 +97,15 @@ def test_outliers_are_exact_powers():
     ratio_rows = ((a[fin] != b[fin]).any(dim=1))
     assert ratio_rows.sum() > 0
     assert torch.equal(a[fin][ratio_rows], b[fin][ratio_rows] * 8)
+
+
+def test_shared_prefix_pages_alias_and_the_rest_are_private():
+    w = inputs.make_workload("shared_prefix_decode")
+    t, ps = w.page_table_np, w.page_size
+    shared = inputs.WORKLOADS["shared_prefix_decode"]["shared_prefix"] // ps
+    assert (t[:, :shared] == t[0, :shared]).all()
+    need = (w.seq_lens_np + ps - 1) // ps
+    private = np.concatenate([t[r, shared:need[r]] for r in range(w.num_seqs)])
+    assert len(np.unique(private)) == len(private)
+    assert not np.isin(private, t[0, :shared]).any()
+    assert not np.isin(w.out_loc_np // ps, t[0, :shared]).any()  # new tokens in private pages
