@@ -45,7 +45,7 @@ def decode_bytes(w) -> int:
     n = w.seq_lens_np.astype(np.int64)
     ps = w.page_size
     kv = int(n.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
-    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * 2
+    qo = 2 * w.num_tokens * w.num_q_heads * w.head_dim * 2   # q_len query rows per request
     meta = int(((n + ps - 1) // ps).sum()) * 4 + 4 * w.num_seqs
     return kv + qo + meta
 
@@ -139,7 +139,10 @@ def _replicate(w, R):
 
 
 def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
-                  fused_store: bool = True):
+                  fused_store: bool = True, via_prefill: bool = False):
+    """Time one workload's attention call.  A multi-token decode workload runs
+    pkv_paged_attn_decode_multi, or with ``via_prefill`` the same batch through
+    pkv_paged_attn_prefill (q_len new tokens after a cached prefix of n - q_len)."""
     import torch
 
     import paged_kv_attention_out_amd as pkv
@@ -147,7 +150,13 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
 
     lib = pkv.lib()
     w = inputs.make_workload(name, device="cuda", poison=False)
+    is_multi = w.kind == "decode" and w.q.dim() == 4
+    if via_prefill:
+        assert is_multi
+        w.q = w.q.reshape(w.num_tokens, w.num_q_heads, w.head_dim)
+        w.kind = "prefill"
     is_decode = w.kind == "decode"
+    L = w.q.shape[1] if is_multi and is_decode else 1
     work_bytes = decode_bytes(w) if is_decode else prefill_bytes(w)
     R = max(1, min(64, math.ceil(MIN_WORKING_SET / max(work_bytes, 1))))
     reps = _replicate(w, R)
@@ -155,6 +164,9 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
     B, Hq, Hkv, d, ps = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
     split = pkv.pkv_decode_split_tokens(B, Hkv, w.max_seq_len, split_tokens) if is_decode else 0
     ws = pkv.decode_workspace(B, Hq, Hkv, d, w.max_seq_len, split_tokens) if is_decode else None
+    if L > 1:
+        nb = pkv.pkv_decode_multi_workspace_bytes(B, L, Hq, Hkv, d, w.max_seq_len, split_tokens)
+        ws = torch.zeros(nb, dtype=torch.uint8, device="cuda") if nb else None
     if not is_decode:
         ws = torch.zeros(pkv.pkv_prefill_workspace_bytes(), dtype=torch.uint8, device="cuda")
     ws_ptr, ws_bytes = (0, 0) if ws is None else (ws.data_ptr(), ws.numel())
@@ -176,6 +188,11 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
                   w.max_seq_len, Hq, Hkv, d, w.scale, split_tokens, out.data_ptr(), ws_ptr,
                   ws_bytes, stream)
             st = None
+        elif L > 1:
+            at = (c.q.data_ptr(), L, c.k_cache.data_ptr(), c.v_cache.data_ptr(), ps,
+                  c.num_pages, c.page_table.data_ptr(), c.page_table.shape[1],
+                  c.seq_lens.data_ptr(), B, w.max_seq_len, Hq, Hkv, d, w.scale, split_tokens,
+                  out.data_ptr(), ws_ptr, ws_bytes, stream)
         elif is_decode:
             at = (c.q.data_ptr(), c.k_cache.data_ptr(), c.v_cache.data_ptr(), ps, c.num_pages,
                   c.page_table.data_ptr(), c.page_table.shape[1], c.seq_lens.data_ptr(), B,
@@ -191,6 +208,7 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
     f_store = lib.pkv_store_kv
     fused = is_decode and w.k_new is not None and fused_store
     f_attn = (lib.pkv_decode_step if fused else
+              lib.pkv_paged_attn_decode_multi if L > 1 else
               lib.pkv_paged_attn_decode if is_decode else lib.pkv_paged_attn_prefill)
 
     def step(i, ev=None):
@@ -515,6 +533,24 @@ def main():
         also["llama_decode_graph_step"] = time_graph_step(args.workload, args.steps,
                                                           args.warmup)
         also["metadata"] = time_metadata(max(20, args.steps // 5))
+        # multi-token decode (4 draft tokens per request), and the same batch
+        # through the prefill kernel for comparison
+        torch.cuda.empty_cache()
+        a = time_workload("spec_decode", max(10, args.steps // 10), max(3, args.warmup // 4))
+        wa = a["workload"]
+        gbs = decode_bytes(wa) / (a["kernel_ms_mean"] * 1e-3) / 1e9
+        also["spec_decode"] = {"GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                               "kernel_us_mean": round(a["kernel_ms_mean"] * 1e3, 2),
+                               "ms_per_step": round(a["ms_per_step"], 4),
+                               "query_tokens_per_s":
+                                   round(wa.num_tokens / (a["ms_per_step"] * 1e-3), 1),
+                               "split_tokens": a["split"], "replicas": a["replicas"]}
+        del a, wa
+        torch.cuda.empty_cache()
+        a = time_workload("spec_decode", max(10, args.steps // 10), max(3, args.warmup // 4),
+                          via_prefill=True)
+        also["spec_decode"]["via_prefill_kernel_us_mean"] = round(a["kernel_ms_mean"] * 1e3, 2)
+        del a
         line["also"] = also
         line["tokens_per_s"] = round(w.num_seqs / (r["ms_per_step"] * 1e-3), 1)
     if not args.no_cpu_baseline:

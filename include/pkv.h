@@ -190,6 +190,56 @@ int pkv_decode_step(const void* q, const void* k_new, const void* v_new,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_decode_multi_workspace_bytes -- size of the workspace
+ * pkv_paged_attn_decode_multi needs (0 when every request fits one split,
+ * and on invalid arguments).  Pass the same split_tokens as to the call.
+ */
+size_t pkv_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_seq_len,
+                                        int32_t split_tokens);
+
+/*
+ * pkv_paged_attn_decode_multi -- q_len query tokens per request, each
+ * attending causally to the context up to its own position.
+ *
+ * This is the decode step of speculative decoding's verification, where a
+ * request feeds a few draft tokens at once instead of one (zero-to-sglang
+ * Part II Ch.1, section 4, roadmap: speculative decoding; the causal rule
+ * with cached tokens is that of prefill, miniVLLM "Engine Architecture",
+ * prepare_prefill).  seq_lens[r] = n counts every token including the q_len
+ * new ones, whose K/V rows must already be in the pool (pkv_store_kv with
+ * q_len rows per request).  Query token t of request r sits at position
+ * n - q_len + t and, for every query head h,
+ *
+ *   out[r, t, h, :] = softmax_j( softmax_scale * <q[r,t,h], K[r, j, h/g]> ) V[r, j, h/g]
+ *
+ * over j = 0 .. n - q_len + t.  With q_len = 1 this is pkv_paged_attn_decode.
+ * A token with no visible key (position < 0, when n < q_len) and every
+ * token of a request with n <= 0 get an all-zero output row.
+ *
+ *   q            : [num_seqs, q_len, num_q_heads, head_dim] bf16
+ *   q_len        : 1 .. 16.  A block of the kernel takes up to 16 / g query
+ *                  tokens of one KV head; longer drafts run in several
+ *                  blocks per KV head, each reading the context again
+ *                  (mostly from L2).  Longer query runs are prefill's shape.
+ *   out          : [num_seqs, q_len, num_q_heads, head_dim] bf16
+ *   workspace    : at least pkv_decode_multi_workspace_bytes(...) bytes,
+ *                  256-byte aligned (contents on entry do not matter).
+ *   all others   : as pkv_paged_attn_decode.
+ *
+ * Errors as pkv_paged_attn_decode; q_len outside 1 .. 16 -> PKV_EINVAL.
+ */
+int pkv_paged_attn_decode_multi(const void* q, int32_t q_len, const void* k_cache,
+                                const void* v_cache, int32_t page_size, int64_t num_pages,
+                                const int32_t* page_table, int32_t page_table_stride,
+                                const int32_t* seq_lens, int32_t num_seqs,
+                                int32_t max_seq_len, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                float softmax_scale, int32_t split_tokens, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pkv_paged_attn_prefill -- causal attention of a flat ragged batch of new
  * tokens over their cached prefix and themselves.
  *

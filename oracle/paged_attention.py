@@ -36,6 +36,13 @@ What it computes, step by step, with the passage each step follows:
 5. ``attend`` -- textbook scaled dot-product attention on the gathered rows:
    ``softmax(scale * q k^T + mask) v``.  The pages name attention but never
    write out its formula; this is the standard definition.
+6. ``decode_multi`` -- a decode step that feeds L tokens per request at once
+   (the verification step of speculative decoding, zero-to-sglang Part II
+   Ch.1 section 4, roadmap): the L new tokens are the last L of the
+   request's ``seq_len`` tokens, and step 4's causal rule applies with a
+   cached prefix of ``seq_len - L``.  Reading where the pages are silent: a
+   token whose position would be negative (seq_len < L) sees no key and,
+   like an empty request, gets an all-zero row.
 
 Every function here is pinned by tests against things other than itself:
 a library routine (torch's scaled_dot_product_attention in float64 on
@@ -221,4 +228,29 @@ def prefill_dense(q: np.ndarray, cu_seqlens_q: np.ndarray, prefix_lens: np.ndarr
         for h in (range(Hq) if heads is None else heads):
             kvh = kv_head_of(h, Hq, Hkv)
             out[s0:s1, h] = attend(qr[:, h], kr[:, kvh], vr[:, kvh], P, scale)
+    return out
+
+
+def decode_multi(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                 page_table: np.ndarray, seq_lens: np.ndarray, scale: float) -> np.ndarray:
+    """``q`` ``[B, L, Hq, d]`` (bf16 bits): new token t of request r sits at
+    position ``seq_lens[r] - L + t`` and attends causally to the pool rows up
+    to there (step 6).  Returns ``[B, L, Hq, d]`` float64; rows with no
+    visible key, and every row of a request with ``seq_lens[r] <= 0``, are
+    zero."""
+    B, L, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    out = np.zeros((B, L, Hq, d))
+    for r in range(B):
+        n = int(seq_lens[r])
+        if n <= 0:
+            continue
+        first = n - L                     # position of new token 0
+        t0 = max(0, -first)               # first token with a non-negative position
+        kr = gather(k_cache, page_table[r], n)
+        vr = gather(v_cache, page_table[r], n)
+        qr = bf16_to_f64(q[r, t0:])
+        for h in range(Hq):
+            kvh = kv_head_of(h, Hq, Hkv)
+            out[r, t0:, h] = attend(qr[:, h], kr[:, kvh], vr[:, kvh], first + t0, scale)
     return out

@@ -11,9 +11,11 @@ from ._lib import (  # noqa: F401
     lib,
     pkv_decode_split_tokens,
     pkv_decode_metadata,
+    pkv_decode_multi_workspace_bytes,
     pkv_decode_step,
     pkv_decode_workspace_bytes,
     pkv_paged_attn_decode,
+    pkv_paged_attn_decode_multi,
     pkv_paged_attn_prefill,
     pkv_prefill_metadata,
     pkv_prefill_workspace_bytes,

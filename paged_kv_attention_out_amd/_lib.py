@@ -45,6 +45,10 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
         _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p,
         _c_void_p, _size, _c_void_p]),
+    "pkv_decode_multi_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_decode_multi": (ctypes.c_int, [
+        _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _i32, _c_void_p, _i32,
+        _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p, _c_void_p, _size, _c_void_p]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -189,6 +193,45 @@ def pkv_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         num_pages, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, max_seq_len, Hq,
         Hkv, d, softmax_scale, split_tokens, _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
         "pkv_decode_step")
+    return out
+
+
+def pkv_decode_multi_workspace_bytes(num_seqs: int, q_len: int, num_q_heads: int,
+                                     num_kv_heads: int, head_dim: int, max_seq_len: int,
+                                     split_tokens: int = 0) -> int:
+    return int(lib().pkv_decode_multi_workspace_bytes(num_seqs, q_len, num_q_heads,
+                                                       num_kv_heads, head_dim, max_seq_len,
+                                                       split_tokens))
+
+
+def pkv_paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                page_table: torch.Tensor, seq_lens: torch.Tensor,
+                                max_seq_len: int, softmax_scale: float,
+                                out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None,
+                                split_tokens: int = 0) -> torch.Tensor:
+    """Multi-token decode; q ``[B, q_len, Hq, d]`` -> out ``[B, q_len, Hq, d]``
+    (bf16); query token t of request r sits at position seq_lens[r] - q_len + t."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    _dev(page_table, torch.int32, "page_table")
+    _dev(seq_lens, torch.int32, "seq_lens")
+    B, L, Hq, d = q.shape
+    num_pages, ps, Hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out")
+    if workspace is None:
+        nbytes = pkv_decode_multi_workspace_bytes(B, L, Hq, Hkv, d, max_seq_len, split_tokens)
+        if nbytes:
+            workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode_multi(
+        _ptr(q), L, _ptr(k_cache), _ptr(v_cache), ps, num_pages, _ptr(page_table),
+        page_table.shape[1], _ptr(seq_lens), B, max_seq_len, Hq, Hkv, d, softmax_scale,
+        split_tokens, _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
+        "pkv_paged_attn_decode_multi")
     return out
 
 

@@ -1,7 +1,9 @@
 // Paged decode attention: one query token per request over its whole
 // context, read through the page table (miniVLLM "Engine Architecture",
 // prepare_decode: context_lens + block_tables; mini-sglang "Engine Class",
-// Key Attributes: page_table).
+// Key Attributes: page_table).  The same kernels serve multi-token decode
+// (a few draft tokens per request, causal among themselves: the verification
+// step of speculative decoding, zero-to-sglang Part II Ch.1 section 4).
 //
 // Two kernels on the caller's stream:
 //
@@ -9,8 +11,9 @@
 //   A split is `split` consecutive tokens; a request with n tokens has
 //   ceil(n/split) splits.  The wave walks its tokens 16 at a time ("groups"):
 //   * S^T = K Q^T on MFMA 16x16x32 bf16: each lane's K loads (8 dims of its
-//     token's row per 32-dim block) are the A operand as loaded; the g query
-//     heads sharing the KV head are replicated over the 16 B columns.
+//     token's row per 32-dim block) are the A operand as loaded; the B
+//     columns hold the (query token, query head) pairs of the KV head -- g
+//     heads x LQ tokens, replicated to fill 16 columns.
 //   * Softmax: base 2 with scale * log2(e) folded in, lazy rescaling (only
 //     when a score exceeds the running max by more than kTau, so p <= 2^kTau;
 //     the function is unchanged, only the reference point moves).
@@ -20,7 +23,7 @@
 //   * K/V rows of a chunk of groups are loaded together, then computed.
 //   * A request with one split writes bf16 output directly; otherwise the
 //     split writes (m, l, un-normalised o) to the workspace.
-// decode_combine_kernel -- one wavefront per (r, query head) with >= 2
+// decode_combine_kernel -- one wavefront per (r, query token, query head) with >= 2
 //   splits merges the partials (flash-decoding): M = max m_s,
 //   L = sum l_s 2^(m_s-M), out = sum o_s 2^(m_s-M) / L.
 //
@@ -69,6 +72,8 @@ struct DecodeParams {
   int32_t max_seq_len;
   int32_t split;
   int32_t n_split_max;
+  int32_t q_len;     // query tokens per request (1 for plain decode)
+  int32_t q_slices;  // blocks per (request, KV head, split): each takes LQ query tokens
   float scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -133,24 +138,32 @@ struct DecodeTraits {
 //   column 4*(L%4) gives every lane 4 consecutive keys of one dim.
 //   O (16 head rows x D dims) lives in D/16 accumulators of 4 registers;
 //   row 4c+i is query head i % G.
-template <int D, int G>
+template <int D, int G, int LQ>
 __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
   constexpr int KCH = D / 32;  // 16-byte pieces per lane per row == QK MFMAs per group
   constexpr int NT = D / 16;   // 16-dim tiles of the output == PV MFMAs per pair
   constexpr int NBUF = DecodeTraits<D, G>::NBUF;
   constexpr int VPITCH = D + 8;  // LDS row pitch (bf16): conflict-free rows
+  constexpr int NC = G * LQ;     // distinct query columns: (query token, query head)
   static_assert(G == 1 || G == 2 || G == 4, "query heads per KV head");
+  static_assert(NC <= 16 && (16 % NC) == 0, "the 16 MFMA columns hold whole copies of the columns");
   __shared__ __attribute__((aligned(16))) uint16_t vlds[NBUF * 16 * VPITCH];
 
   const int lane = threadIdx.x;
-  // Block -> unit: rank = block / Hkv walks the (request, split) pairs that
+  // Block -> unit: rank = block / (Hkv * slices) walks the (request, split) pairs that
   // exist -- request-major, each request with max(ceil(n / split), 1)
   // splits -- so every block of the grid past the last pair sits at its end
   // and the dispatcher starts real units first.  The KV head is the fastest
   // index: the heads of one (request, split) sweep the same pages together.
   // It rotates from one rank to the next because blocks land on the 8 XCDs
   // round-robin: every XCD then sees every head's offset within the page rows.
-  const uint32_t rank = blockIdx.x / (uint32_t)p.num_kv_heads;
+  // With several query slices (multi-token queries wider than the 16 MFMA
+  // columns) the slices of one unit are Hkv blocks apart: with Hkv a
+  // multiple of 8 they share an XCD, so the second slice reads K/V from L2.
+  const uint32_t u = blockIdx.x / (uint32_t)p.num_kv_heads;
+  const uint32_t rank = LQ == 1 ? u : u / (uint32_t)p.q_slices;
+  const int tq0 = LQ == 1 ? 0 : (int)(u % (uint32_t)p.q_slices) * LQ;  // first query token
+  const int QL = LQ == 1 ? 1 : p.q_len;
 #ifdef PKV_DECODE_NO_ROTATE
   const int kvh = (int)(blockIdx.x % (uint32_t)p.num_kv_heads);
 #else
@@ -189,13 +202,19 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   const int64_t rk = (int64_t)r * p.num_kv_heads + kvh;
   const int j = lane & 15;  // token within the group / score column
   const int c = lane >> 4;  // 16-byte piece within each 64-byte block / token quad
-  const int hcol = j % G;   // query head of this lane's score column
+  const int col = j % NC;   // logical column of this lane: query token col / G, head col % G
+  const int hcol = col % G;
+  // Query token of the column; columns past the last token repeat it and
+  // are never written.
+  const int tq = min(tq0 + col / G, QL - 1);
   const int t_begin = split * p.split;
 
-  // Q^T fragments (B operand): column j holds head kvh*G + j % G.
+  // Q^T fragments (B operand): column j holds query token tq of head
+  // kvh*G + hcol (the NC columns repeat over the 16 MFMA columns).
   bf16x8 qb[KCH];
   {
-    const uint16_t* qp = p.q + ((int64_t)r * p.num_q_heads + (int64_t)kvh * G + hcol) * D + 8 * c;
+    const uint16_t* qp =
+        p.q + (((int64_t)r * QL + tq) * p.num_q_heads + (int64_t)kvh * G + hcol) * D + 8 * c;
 #pragma unroll
     for (int kk = 0; kk < KCH; ++kk) qb[kk] = as_bf16x8(ld16(qp + 32 * kk));
   }
@@ -214,11 +233,16 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   };
   load_window(t_begin >> p.page_shift);
 
-  uint16_t* out_rk = p.out + ((int64_t)r * p.num_q_heads + (int64_t)kvh * G) * D;
   if (n <= 0) {
-    if (split == 0)
-      for (int i = lane; i < G * D / 8; i += 64)
-        reinterpret_cast<uint4*>(out_rk)[i] = make_uint4(0, 0, 0, 0);
+    if (split == 0) {
+#pragma unroll
+      for (int t = tq0; t < tq0 + LQ; ++t) {
+        if (t >= QL) break;
+        uint16_t* row = p.out + (((int64_t)r * QL + t) * p.num_q_heads + (int64_t)kvh * G) * D;
+        for (int i = lane; i < G * D / 8; i += 64)
+          reinterpret_cast<uint4*>(row)[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
     return;
   }
   const int ns = (n + p.split - 1) / p.split;
@@ -228,7 +252,7 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   // Fused step: the request's last split writes this head's slice of the
   // new token's K/V rows to slot out_loc[r] (out-of-range slots are
   // skipped).  No wave of this call reads that slot from the pool.
-  if (p.k_new != nullptr && split == ns - 1 && lane < D / 8) {
+  if (LQ == 1 && p.k_new != nullptr && split == ns - 1 && lane < D / 8) {
     const int64_t slot = p.out_loc[r];
     if (slot >= 0 && slot < p.num_slots) {
       const int64_t src = ((int64_t)r * p.num_kv_heads + kvh) * D + 8 * lane;
@@ -248,7 +272,7 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
 
   // Fused step: the lane whose token is the new one (position n - 1) reads
   // its row from k_new / v_new instead of the pool.
-  const int t_new = p.k_new != nullptr ? n - 1 : -1;
+  const int t_new = LQ == 1 && p.k_new != nullptr ? n - 1 : -1;
   const int64_t new_off = ((int64_t)r * p.num_kv_heads + kvh) * D + 8 * c;
 
   uint4 kb[NBUF][KCH], vb[NBUF][KCH];
@@ -300,17 +324,20 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   f32x4 o[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_all[G];  // running max per query head, the same in every lane
-#pragma unroll
-  for (int h = 0; h < G; ++h) m_all[h] = kNegInf;
-  float m_own = kNegInf;  // m_all[hcol]
-  float l_own = 0.f;      // this lane's share of the row sum of head hcol
+  float m_own = kNegInf;  // running max of this lane's column (equal in all its lanes)
+  float l_own = 0.f;      // this lane's share of the row sum of its column
+  // Query token tq sits at position n - QL + tq and sees keys up to there;
+  // lim_lo is the lowest limit among this block's columns.
+  const int lim = n - QL + tq;
+  const int lim_lo = n - QL + tq0;
 
   const int trq = j & 3, trj = j >> 2;  // transpose-read lane roles
 
   // One pair of groups: softmax of the 32 scores, then O += P V.
-  // va / vbv: valid tokens of each group (0 = absent group).
-  auto pv_pair = [&](f32x4 sa, f32x4 sb, int va, int vbv, int slot_a, int slot_b) {
+  // va / vbv: valid tokens of each group (0 = absent group); ta / tb: the
+  // groups' first positions (for the causal limit of multi-token queries).
+  auto pv_pair = [&](f32x4 sa, f32x4 sb, int va, int vbv, int slot_a, int slot_b, int ta,
+                     int tb) {
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -324,38 +351,43 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
         x[4 + i] = 4 * c + i < vbv ? x[4 + i] : kNegInf;
       }
     }
+    if (LQ > 1 && tb + 15 > lim_lo) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = ta + 4 * c + i <= lim ? x[i] : kNegInf;
+        x[4 + i] = tb + 4 * c + i <= lim ? x[4 + i] : kNegInf;
+      }
+    }
     float lm = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
     if (__any(lm > m_own + kTau)) {
-      // new running max of every head: max over the lanes holding it
-      float alpha[G];
+      // New running max of each column: over the lanes that hold it -- the
+      // four token quads (lane ^ 16, ^ 32) and the copies of the column
+      // among the 16 MFMA columns (lane ^ NC, ^ 2NC, ...).
+      float v = fmaxf(lm, __shfl_xor(lm, 16));
+      v = fmaxf(v, __shfl_xor(v, 32));
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float v = hcol == h ? lm : kNegInf;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-        const float mn = fmaxf(m_all[h], v);
-        alpha[h] = mn == kNegInf ? 0.f : fast_exp2(m_all[h] - mn);
-        m_all[h] = mn;
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[t][i] *= alpha[i % G];
-      float a_own = alpha[0];
-      m_own = m_all[0];
-#pragma unroll
-      for (int h = 1; h < G; ++h) {
-        a_own = hcol == h ? alpha[h] : a_own;
-        m_own = hcol == h ? m_all[h] : m_own;
-      }
+      for (int off = NC; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+      const float mn = fmaxf(m_own, v);
+      const float a_own = mn == kNegInf ? 0.f : fast_exp2(m_own - mn);
+      m_own = mn;
       l_own *= a_own;
+      // O row 4c+i is column (4c+i) % NC, whose factor lane (4c+i) % NC holds.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ar = __shfl(a_own, (4 * c + i) % NC);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[t][i] *= ar;
+      }
     }
+    // A multi-token column with no visible key yet keeps m = -inf: subtract
+    // 0 instead so its probabilities come out 0, not NaN.
+    const float m_sub = LQ > 1 && m_own == kNegInf ? 0.f : m_own;
     float e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      e[i] = fast_exp2(x[i] - m_own);
+      e[i] = fast_exp2(x[i] - m_sub);
       l_own += e[i];
     }
     uint4 pw;
@@ -398,7 +430,7 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
         const f32x4 sa = scores(b), sb = scores(b + 1);
         stage_v(b, b);
         stage_v(b + 1, b + 1);
-        pv_pair(sa, sb, 16, 16, b, b + 1);
+        pv_pair(sa, sb, 16, 16, b, b + 1, w0 + 16 * (g + b), w0 + 16 * (g + b + 1));
       }
     }
     // Remaining full groups and the tail, two groups at a time; an absent
@@ -420,41 +452,42 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
       }
       const f32x4 sa = scores(0);
       stage_v(0, 0);
-      pv_pair(sa, sb, va, vbv, 0, 1);
+      pv_pair(sa, sb, va, vbv, 0, 1, w0 + 16 * g, w0 + 16 * (g + 1));
     }
   }
 
   // Row sums: a column's keys are spread over the four token quads.
   float l_tot = l_own + __shfl_xor(l_own, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  float L[G];
+  // O row x = 4c + i (query column x % NC) sits in lanes 16c .. 16c+15, dim
+  // 16t + lane % 16; lane x holds column x's max and sum.
+  if (4 * c >= NC) return;  // rows 4c.. hold no column of their own
+  const int dl = lane & 15;
 #pragma unroll
-  for (int h = 0; h < G; ++h) L[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_tot), h));
-  if (lane >= 16) return;  // lanes 0..15 hold head rows 0..3, dims 16t + lane
-
-  if (ns == 1) {
+  for (int i = 0; i < 4; ++i) {
+    const int x = 4 * c + i;
+    const float Lx = __shfl(l_tot, x % NC);
+    const float Mx = __shfl(m_own, x % NC);
+    const int h = x % G, tx = tq0 + x / G;
+    if (x >= NC || tx >= QL) continue;
+    if (ns == 1) {
+      // (a multi-token row with no visible key has L = 0 and gets zeros)
+      const float inv = LQ > 1 && Lx == 0.f ? 0.f : 1.f / Lx;
+      uint16_t* o_row =
+          p.out + (((int64_t)r * QL + tx) * p.num_q_heads + (int64_t)kvh * G + h) * D;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float inv = 1.f / L[h];
+      for (int t = 0; t < NT; ++t) o_row[16 * t + dl] = to_bf16(o[t][i] * inv);
+    } else {
+      // Partial (m, l, un-normalised o) of this split for column (tx, h)
+      // among the QL * G columns of the request's KV head.
+      const int64_t base = (rk * p.n_split_max + split) * (QL * G) + tx * G + h;
+      float* dst = p.ws_o + base * D + dl;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) out_rk[h * D + 16 * t + lane] = to_bf16(o[t][h] * inv);
-    }
-    return;
-  }
-
-  // Partial (m, l, un-normalised o) of this split.
-  const int64_t base = (rk * p.n_split_max + split) * G;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float* dst = p.ws_o + (base + h) * D + lane;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dst[16 * t] = o[t][h];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      p.ws_m[base + h] = m_all[h];
-      p.ws_l[base + h] = L[h];
+      for (int t = 0; t < NT; ++t) dst[16 * t] = o[t][i];
+      if (dl == 0) {
+        p.ws_m[base] = Mx;
+        p.ws_l[base] = Lx;
+      }
     }
   }
 }
@@ -469,27 +502,33 @@ constexpr int kCombineBatch = 16;  // splits whose o rows are in flight together
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   constexpr int DPL = D / 64;  // output dims per lane
+  const int QL = p.q_len;
+  const int NC = G * QL;  // partial columns per (request, KV head, split)
   const int lane = threadIdx.x & 63;
-  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (request, query head)
-  if (rh >= (int64_t)p.num_seqs * p.num_q_heads) return;
-  const int r = (int)(rh / p.num_q_heads);
-  const int qh = (int)(rh % p.num_q_heads);
+  // one wave per (request, query token, query head)
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rh >= (int64_t)p.num_seqs * QL * p.num_q_heads) return;
+  const int r = (int)(rh / ((int64_t)QL * p.num_q_heads));
+  const int rem = (int)(rh % ((int64_t)QL * p.num_q_heads));
+  const int tq = rem / p.num_q_heads;
+  const int qh = rem % p.num_q_heads;
   const int kvh = qh / G, h = qh % G;
+  const int x = tq * G + h;  // column
   const int nsm = p.n_split_max;
   const int64_t sbase = ((int64_t)r * p.num_kv_heads + kvh) * nsm;  // split 0
-  const float* om = p.ws_m + sbase * G + h;
-  const float* ol = p.ws_l + sbase * G + h;
-  const float* oo = p.ws_o + sbase * G * D + (int64_t)h * D + lane;
+  const float* om = p.ws_m + sbase * NC + x;
+  const float* ol = p.ws_l + sbase * NC + x;
+  const float* oo = p.ws_o + (sbase * NC + x) * D + lane;
 
   int n = p.seq_lens[r];
   // First batch of partials, issued together with the length.
-  float mv = lane < nsm ? om[(int64_t)lane * G] : kNegInf;
-  float lv = lane < nsm ? ol[(int64_t)lane * G] : 0.f;
+  float mv = lane < nsm ? om[(int64_t)lane * NC] : kNegInf;
+  float lv = lane < nsm ? ol[(int64_t)lane * NC] : 0.f;
   float v[kCombineBatch][DPL];
 #pragma unroll
   for (int k = 0; k < kCombineBatch; ++k)
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) v[k][i] = k < nsm ? oo[(int64_t)k * G * D + 64 * i] : 0.f;
+    for (int i = 0; i < DPL; ++i) v[k][i] = k < nsm ? oo[(int64_t)k * NC * D + 64 * i] : 0.f;
 
   n = uniform(n);
   n = n > p.max_seq_len ? p.max_seq_len : n;
@@ -500,19 +539,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   // Global max over the splits (lane s holds split s, 64 at a time).
   float M = kNegInf;
   for (int s0 = 0; s0 < ns; s0 += 64) {
-    float x = s0 + lane < ns ? (s0 == 0 ? mv : om[(int64_t)(s0 + lane) * G]) : kNegInf;
+    float y = s0 + lane < ns ? (s0 == 0 ? mv : om[(int64_t)(s0 + lane) * NC]) : kNegInf;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    M = fmaxf(M, x);
+    for (int off = 32; off >= 1; off >>= 1) y = fmaxf(y, __shfl_xor(y, off));
+    M = fmaxf(M, y);
   }
+  // (a multi-token row with no visible key: every m is -inf, every l is 0)
+  if (M == kNegInf) M = 0.f;
   float L = 0.f, acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   for (int s0 = 0; s0 < ns; s0 += 64) {
     const int s = s0 + lane;
-    const float ms = s < ns ? (s0 == 0 ? mv : om[(int64_t)s * G]) : kNegInf;
+    const float ms = s < ns ? (s0 == 0 ? mv : om[(int64_t)s * NC]) : kNegInf;
     const float w = s < ns ? fast_exp2(ms - M) : 0.f;
-    float t = s < ns ? (s0 == 0 ? lv : ol[(int64_t)s * G]) * w : 0.f;
+    float t = s < ns ? (s0 == 0 ? lv : ol[(int64_t)s * NC]) * w : 0.f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
     L += t;
@@ -524,7 +565,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
         for (int k = 0; k < kCombineBatch; ++k)
 #pragma unroll
           for (int i = 0; i < DPL; ++i)
-            v[k][i] = k0 + k < cnt ? oo[(int64_t)(s0 + k0 + k) * G * D + 64 * i] : 0.f;
+            v[k][i] = k0 + k < cnt ? oo[(int64_t)(s0 + k0 + k) * NC * D + 64 * i] : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < kCombineBatch; ++k) {
@@ -536,8 +577,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
       }
     }
   }
-  uint16_t* out = p.out + rh * D;
-  const float inv = 1.f / L;
+  uint16_t* out = p.out + (((int64_t)r * QL + tq) * p.num_q_heads + qh) * D;
+  const float inv = L == 0.f ? 0.f : 1.f / L;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) out[lane + 64 * i] = to_bf16(acc[i] * inv);
 }
@@ -566,13 +607,27 @@ struct WsLayout {
   size_t m, l, o, total;
 };
 
-WsLayout ws_layout(int64_t rk, int64_t nsm, int g, int d) {
+// ncols = query columns per (request, KV head): g * q_len
+WsLayout ws_layout(int64_t rk, int64_t nsm, int64_t ncols, int d) {
   WsLayout w;
   w.m = 0;
-  w.l = w.m + align256(rk * nsm * g * sizeof(float));
-  w.o = w.l + align256(rk * nsm * g * sizeof(float));
-  w.total = w.o + align256(rk * nsm * g * d * sizeof(float));
+  w.l = w.m + align256(rk * nsm * ncols * sizeof(float));
+  w.o = w.l + align256(rk * nsm * ncols * sizeof(float));
+  w.total = w.o + align256(rk * nsm * ncols * d * sizeof(float));
   return w;
+}
+
+// Query tokens per request handled by one multi-token launch; longer query
+// runs are prefill's shape.
+constexpr int kMaxQueryLen = 16;
+
+// Query tokens per block for q_len tokens and g heads per KV head: the
+// smallest power of two >= q_len, capped so that g * LQ fits the 16 MFMA
+// columns.
+int query_tile(int q_len, int g) {
+  int lq = 1;
+  while (lq < q_len) lq *= 2;
+  return lq * g > 16 ? 16 / g : lq;
 }
 
 bool decode_shape_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -585,14 +640,30 @@ bool decode_shape_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
   return true;
 }
 
-template <int D, int G>
+template <int D, int G, int LQ>
 int launch_decode(const DecodeParams& p, int64_t blocks, hipStream_t s) {
-  const int st = pkv_host::launch(decode_split_kernel<D, G>, dim3((unsigned)blocks), dim3(64),
-                                  s, p);
+  const int st = pkv_host::launch(decode_split_kernel<D, G, LQ>, dim3((unsigned)blocks),
+                                  dim3(64), s, p);
   if (st != PKV_OK || p.n_split_max <= 1) return st;
-  const int64_t cblocks = ((int64_t)p.num_seqs * p.num_q_heads + 3) / 4;
+  const int64_t cblocks = ((int64_t)p.num_seqs * p.q_len * p.num_q_heads + 3) / 4;
   return pkv_host::launch(decode_combine_kernel<D, G>, dim3((unsigned)cblocks), dim3(256), s,
                           p);
+}
+
+template <int D, int G>
+int launch_decode_lq(const DecodeParams& p, int lq, int64_t blocks, hipStream_t s) {
+  switch (lq) {
+    case 1: return launch_decode<D, G, 1>(p, blocks, s);
+    case 2: return launch_decode<D, G, 2>(p, blocks, s);
+    case 4: return launch_decode<D, G, 4>(p, blocks, s);
+    case 8:
+      if constexpr (G <= 2) return launch_decode<D, G, 8>(p, blocks, s);
+      break;
+    case 16:
+      if constexpr (G == 1) return launch_decode<D, G, 16>(p, blocks, s);
+      break;
+  }
+  return PKV_EUNSUPPORTED;
 }
 
 }  // namespace
@@ -618,12 +689,29 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
       .total;
 }
 
+extern "C" size_t pkv_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len,
+                                                   int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim, int32_t max_seq_len,
+                                                   int32_t split_tokens) {
+  if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                       split_tokens))
+    return 0;
+  if (q_len < 1 || q_len > kMaxQueryLen) return 0;
+  const int32_t s = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
+  const int64_t nsm = (max_seq_len + s - 1) / s;
+  if (nsm <= 1 || num_seqs == 0) return 0;
+  return ws_layout((int64_t)num_seqs * num_kv_heads, nsm,
+                   (int64_t)q_len * (num_q_heads / num_kv_heads), head_dim)
+      .total;
+}
+
 namespace {
 
 int decode_impl(const void* q, const void* k_new, const void* v_new, const int32_t* out_loc,
                 const void* k_cache, const void* v_cache, int32_t page_size, int64_t num_pages,
                 const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
-                int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                int32_t num_seqs, int32_t q_len, int32_t max_seq_len, int32_t num_q_heads,
+                int32_t num_kv_heads,
                 int32_t head_dim, float softmax_scale, int32_t split_tokens, void* out,
                 void* workspace, size_t workspace_bytes, void* stream) {
   using namespace pkv_host;
@@ -631,12 +719,14 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
                        split_tokens))
     return PKV_EINVAL;
   if (!finite_positive(softmax_scale)) return PKV_EINVAL;
+  if (q_len < 1 || q_len > kMaxQueryLen) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out) return PKV_EINVAL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return PKV_EINVAL;
   const bool fused = k_new != nullptr || v_new != nullptr || out_loc != nullptr;
-  if (fused && (!k_new || !v_new || !out_loc || !aligned16(k_new) || !aligned16(v_new)))
+  if (fused && (q_len != 1 || !k_new || !v_new || !out_loc || !aligned16(k_new) ||
+                !aligned16(v_new)))
     return PKV_EINVAL;
   if (num_pages <= 0 || page_table_stride <= 0) return PKV_EINVAL;
   if (!is_pow2_page(page_size)) return PKV_EUNSUPPORTED;
@@ -648,9 +738,11 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   const int32_t split = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
   const int64_t nsm = (max_seq_len + split - 1) / split;
   const int64_t rk = (int64_t)num_seqs * num_kv_heads;
+  const int lq = query_tile(q_len, g);
+  const int slices = (q_len + lq - 1) / lq;
   DecodeParams p = {};
   if (nsm > 1) {
-    const WsLayout w = ws_layout(rk, nsm, g, head_dim);
+    const WsLayout w = ws_layout(rk, nsm, (int64_t)g * q_len, head_dim);
     if (workspace_bytes < w.total) return PKV_ENOSPACE;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PKV_EINVAL;
     char* ws = static_cast<char*>(workspace);
@@ -658,9 +750,9 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
     p.ws_l = reinterpret_cast<float*>(ws + w.l);
     p.ws_o = reinterpret_cast<float*>(ws + w.o);
   }
-  // One block per (request, split) pair and KV head, at most units blocks;
-  // blocks past the pairs that exist exit at once.
-  const int64_t blocks = rk * nsm;
+  // One block per (request, split) pair, KV head and query slice, at most
+  // this many; blocks past the pairs that exist exit at once.
+  const int64_t blocks = rk * nsm * slices;
   if (blocks > INT32_MAX) return PKV_EINVAL;
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -686,16 +778,18 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   p.max_seq_len = max_seq_len;
   p.split = split;
   p.n_split_max = (int32_t)nsm;
+  p.q_len = q_len;
+  p.q_slices = slices;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (head_dim == 64) {
-    if (g == 1) return launch_decode<64, 1>(p, blocks, s);
-    if (g == 2) return launch_decode<64, 2>(p, blocks, s);
-    return launch_decode<64, 4>(p, blocks, s);
+    if (g == 1) return launch_decode_lq<64, 1>(p, lq, blocks, s);
+    if (g == 2) return launch_decode_lq<64, 2>(p, lq, blocks, s);
+    return launch_decode_lq<64, 4>(p, lq, blocks, s);
   }
-  if (g == 1) return launch_decode<128, 1>(p, blocks, s);
-  if (g == 2) return launch_decode<128, 2>(p, blocks, s);
-  return launch_decode<128, 4>(p, blocks, s);
+  if (g == 1) return launch_decode_lq<128, 1>(p, lq, blocks, s);
+  if (g == 2) return launch_decode_lq<128, 2>(p, lq, blocks, s);
+  return launch_decode_lq<128, 4>(p, lq, blocks, s);
 }
 
 }  // namespace
@@ -709,7 +803,7 @@ extern "C" int pkv_paged_attn_decode(const void* q, const void* k_cache, const v
                                      float softmax_scale, int32_t split_tokens, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, nullptr, nullptr, nullptr, k_cache, v_cache, page_size, num_pages,
-                     page_table, page_table_stride, seq_lens, num_seqs, max_seq_len,
+                     page_table, page_table_stride, seq_lens, num_seqs, 1, max_seq_len,
                      num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
                      workspace, workspace_bytes, stream);
 }
@@ -724,7 +818,22 @@ extern "C" int pkv_decode_step(const void* q, const void* k_new, const void* v_n
                                size_t workspace_bytes, void* stream) {
   if (num_seqs > 0 && (!k_new || !v_new || !out_loc)) return PKV_EINVAL;
   return decode_impl(q, k_new, v_new, out_loc, k_cache, v_cache, page_size, num_pages,
-                     page_table, page_table_stride, seq_lens, num_seqs, max_seq_len,
+                     page_table, page_table_stride, seq_lens, num_seqs, 1, max_seq_len,
+                     num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
+                     workspace, workspace_bytes, stream);
+}
+
+extern "C" int pkv_paged_attn_decode_multi(const void* q, int32_t q_len, const void* k_cache,
+                                           const void* v_cache, int32_t page_size,
+                                           int64_t num_pages, const int32_t* page_table,
+                                           int32_t page_table_stride, const int32_t* seq_lens,
+                                           int32_t num_seqs, int32_t max_seq_len,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, float softmax_scale,
+                                           int32_t split_tokens, void* out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  return decode_impl(q, nullptr, nullptr, nullptr, k_cache, v_cache, page_size, num_pages,
+                     page_table, page_table_stride, seq_lens, num_seqs, q_len, max_seq_len,
                      num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
                      workspace, workspace_bytes, stream);
 }

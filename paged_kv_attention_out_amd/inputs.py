@@ -63,6 +63,11 @@ WORKLOADS = {
         kind="decode", num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=64,
         page_size=16, len_range=(1024 + 64, 1024 + 1024), shared_prefix=1024,
         store_new=True, seed=1006),
+    # Llama-shaped decode feeding 4 tokens per request at once (speculative
+    # decoding's verification step); the 4 tokens are already in the pool.
+    "spec_decode": dict(
+        kind="decode", num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=64,
+        page_size=16, len_range=(128, 2048), q_len=4, store_new=False, seed=1007),
 }
 
 POOL_FACTOR = 1.25
@@ -86,11 +91,11 @@ class Workload:
     poison_page: int
     scale: float
     seq_lens_np: np.ndarray        # [B] total tokens visible to the last query
-    prefix_lens_np: np.ndarray     # [B] cached tokens (prefill); n-1 (decode)
+    prefix_lens_np: np.ndarray     # [B] cached tokens (prefill); n - q_len (decode)
     q_lens_np: np.ndarray          # [B] new tokens per request
     page_table_np: np.ndarray      # [B, W]
     out_loc_np: Optional[np.ndarray]
-    q: torch.Tensor                # [B, Hq, d] (decode) or [T, Hq, d] (prefill)
+    q: torch.Tensor                # [B, Hq, d] or [B, q_len, Hq, d] (decode); [T, Hq, d] (prefill)
     k_cache: torch.Tensor          # [num_pages, ps, Hkv, d] bf16
     v_cache: torch.Tensor
     k_new: Optional[torch.Tensor]  # [T_new, Hkv, d] bf16 rows to store
@@ -215,10 +220,13 @@ def _poison(cache: torch.Tensor, table: np.ndarray, seq_lens: np.ndarray,
 def build_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                  seq_lens, *, seed, device="cpu", pool_pages=None, width=None,
                  store_new=False, outlier_frac=0.0, outlier_scale=8.0,
-                 poison=True, name="custom_decode", shared_pages=0) -> Workload:
+                 poison=True, name="custom_decode", shared_pages=0, q_len=1) -> Workload:
     """Decode batch: one query per request at position n_r - 1 attending to
     all n_r tokens.  With ``store_new`` the token at n_r - 1 is not yet in the
-    pool: its K/V rows come in ``k_new``/``v_new`` with slots ``out_loc``."""
+    pool: its K/V rows come in ``k_new``/``v_new`` with slots ``out_loc``.
+    With ``q_len`` > 1, q is ``[B, q_len, Hq, d]``: the last q_len tokens of
+    each request, all already in the pool."""
+    assert q_len >= 1 and not (store_new and q_len > 1)
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     assert len(seq_lens) == num_seqs
@@ -231,7 +239,9 @@ def build_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
     shape = (pool + 1, ps, num_kv_heads, head_dim)
     k_cache = _randn_bf16(shape, gen, device)
     v_cache = _randn_bf16(shape, gen, device)
-    q = _randn_bf16((num_seqs, num_q_heads, head_dim), gen, device)
+    q_shape = (num_seqs, num_q_heads, head_dim) if q_len == 1 else \
+        (num_seqs, q_len, num_q_heads, head_dim)
+    q = _randn_bf16(q_shape, gen, device)
     k_new = v_new = out_loc = out_loc_np = None
     if store_new:
         k_new = _randn_bf16((num_seqs, num_kv_heads, head_dim), gen, device)
@@ -251,8 +261,8 @@ def build_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
         _poison(v_cache, table, seq_lens, ps, pool, out_loc_np)
     if out_loc_np is not None:
         out_loc = torch.from_numpy(out_loc_np).to(device)
-    prefix = np.maximum(seq_lens - 1, 0).astype(np.int32)
-    qlens = np.ones(num_seqs, dtype=np.int32)
+    prefix = np.maximum(seq_lens - q_len, 0).astype(np.int32)
+    qlens = np.full(num_seqs, q_len, dtype=np.int32)
     cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
     return Workload(
         name=name, kind="decode", seed=seed, num_seqs=num_seqs,
@@ -349,7 +359,8 @@ def make_workload(name: str, *, seed: Optional[int] = None, device="cpu",
             store_new=cfg["store_new"],
             outlier_frac=cfg.get("outlier_frac", 0.0),
             outlier_scale=cfg.get("outlier_scale", 8.0), poison=poison,
-            name=name, shared_pages=cfg.get("shared_prefix", 0) // ps)
+            name=name, shared_pages=cfg.get("shared_prefix", 0) // ps,
+            q_len=cfg.get("q_len", 1))
     prefix, qlens = draw_lengths(name, seed)
     width = -(-(cfg["prefix_range"][1] + cfg["new_range"][1]) // ps)
     return build_prefill(

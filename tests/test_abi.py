@@ -115,6 +115,41 @@ def test_decode_step_validation(kw, status):
     assert _step(**kw) == status
 
 
+def _multi(**kw):
+    a = dict(q=FAKE, L=4, kc=FAKE, vc=FAKE, ps=16, pages=100, pt=FAKE, stride=128, seq=FAKE,
+             B=4, maxlen=2048, hq=32, hkv=8, d=64, scale=0.125, split=0, out=FAKE, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_paged_attn_decode_multi(
+        a["q"], a["L"], a["kc"], a["vc"], a["ps"], a["pages"], a["pt"], a["stride"], a["seq"],
+        a["B"], a["maxlen"], a["hq"], a["hkv"], a["d"], a["scale"], a["split"], a["out"],
+        a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), 1), (dict(L=17), 1), (dict(L=-3), 1), (dict(q=None), 1), (dict(out=None), 1),
+    (dict(seq=None), 1), (dict(scale=0.0), 1), (dict(hq=30), 1), (dict(split=24), 1),
+    (dict(q=FAKE + 2), 1), (dict(d=96), 2), (dict(hq=64), 2), (dict(ps=24), 2),
+    (dict(wsb=100, ws=FAKE), 3), (dict(ws=FAKE + 64, wsb=1 << 30), 1),
+    (dict(B=0), 0), (dict(B=0, L=16), 0),
+])
+def test_decode_multi_validation(kw, status):
+    assert _multi(**kw) == status
+
+
+def test_decode_multi_workspace_sizes():
+    # q_len = 1 needs what plain decode needs
+    for args in ((64, 32, 8, 64, 2048), (16, 16, 16, 128, 4096), (1, 4, 2, 64, 64)):
+        B, hq, hkv, d, maxlen = args
+        assert pkv.pkv_decode_multi_workspace_bytes(B, 1, hq, hkv, d, maxlen) == \
+            pkv.pkv_decode_workspace_bytes(B, hq, hkv, d, maxlen)
+    one = pkv.pkv_decode_multi_workspace_bytes(64, 1, 32, 8, 64, 2048)
+    four = pkv.pkv_decode_multi_workspace_bytes(64, 4, 32, 8, 64, 2048)
+    assert 4 * one - 3 * 256 <= four <= 4 * one   # every array grows by q_len (256-B rounding)
+    assert pkv.pkv_decode_multi_workspace_bytes(64, 0, 32, 8, 64, 2048) == 0
+    assert pkv.pkv_decode_multi_workspace_bytes(64, 17, 32, 8, 64, 2048) == 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(seq=None), 1), (dict(pre=None), 1), (dict(pt=None), 1), (dict(cu=None), 1),
     (dict(loc=None), 1), (dict(B=-1), 1), (dict(maxt=-1), 1), (dict(stride=0), 1),

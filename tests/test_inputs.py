@@ -109,3 +109,22 @@ def test_shared_prefix_pages_alias_and_the_rest_are_private():
     assert len(np.unique(private)) == len(private)
     assert not np.isin(private, t[0, :shared]).any()
     assert not np.isin(w.out_loc_np // ps, t[0, :shared]).any()  # new tokens in private pages
+
+
+def test_multi_token_decode_inputs():
+    w = inputs.build_decode(3, 8, 2, 16, 16, [2, 40, 17], seed=21, q_len=4)
+    _check_pages(w)
+    assert tuple(w.q.shape) == (3, 4, 8, 16)
+    assert w.q_lens_np.tolist() == [4, 4, 4] and w.num_tokens == 12
+    assert w.prefix_lens_np.tolist() == [0, 36, 13]
+    # every owned position, the new tokens included, holds finite K/V
+    for r in range(3):
+        for t in range(int(w.seq_lens_np[r])):
+            row = w.k_cache[w.page_table_np[r, t // 16], t % 16]
+            assert torch.isfinite(row.float()).all()
+    # q_len = 1 keeps the single-token layout and random stream
+    a = inputs.build_decode(3, 8, 2, 16, 16, [2, 40, 17], seed=21)
+    b = inputs.build_decode(3, 8, 2, 16, 16, [2, 40, 17], seed=21, q_len=1)
+    assert torch.equal(a.q, b.q) and tuple(a.q.shape) == (3, 8, 16)
+    with pytest.raises(AssertionError):
+        inputs.build_decode(3, 8, 2, 16, 16, [2, 40, 17], seed=21, q_len=2, store_new=True)

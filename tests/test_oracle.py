@@ -7,7 +7,8 @@
   returns that row, one visible key returns its V row, two keys give the
   logistic weights, a huge scale gives the arg-max row);
 * invariants (physical page permutation, GQA as MHA with repeated K/V
-  heads, chunked prefill vs. one long prefill, decode as a one-row prefill);
+  heads, chunked prefill vs. one long prefill, decode as a one-row prefill,
+  multi-token decode with one token as decode);
 * the pages' one worked value: cu_seqlens_q = [0, 5, 8, 12];
 * planted mistakes: each plausible slip in the oracle must trip a pin.
 """
@@ -282,6 +283,39 @@ def pin_golden_cu_seqlens():
     np.testing.assert_allclose(got, c.sdpa(), rtol=1e-12, atol=1e-12)
 
 
+def pin_decode_multi_vs_sdpa(seed=17):
+    L = 4
+    c = Case(seed, Hq=8, Hkv=2, d=16, ps=16, prefix=[0, 12, 29, 60], qlens=[L] * 4)
+    got = orc.decode_multi(c.q.reshape(4, L, 8, 16), c.k_cache, c.v_cache, c.table, c.n,
+                           c.scale)
+    np.testing.assert_allclose(got, c.sdpa().reshape(4, L, 8, 16), rtol=1e-12, atol=1e-12)
+
+
+def pin_decode_multi_one_token_is_decode(seed=18):
+    c = Case(seed, Hq=4, Hkv=2, d=8, ps=16, prefix=[0, 7, 31], qlens=[1, 1, 1])
+    one = orc.decode_multi(c.q.reshape(3, 1, 4, 8), c.k_cache, c.v_cache, c.table, c.n,
+                           c.scale)
+    dec = orc.decode(c.q.reshape(3, 4, 8), c.k_cache, c.v_cache, c.table, c.n, c.scale)
+    assert np.isfinite(dec).all()
+    np.testing.assert_allclose(one[:, 0], dec, rtol=0, atol=0)
+
+
+def pin_decode_multi_short_context(seed=19):
+    # 3 tokens in the pool but 5 query rows: rows 0 and 1 would sit at
+    # positions -2 and -1 and see nothing (zeros); rows 2..4 are the three
+    # tokens' causal attention; an empty request is all zero.
+    c = Case(seed, Hq=4, Hkv=2, d=8, ps=16, prefix=[0], qlens=[3])
+    extra = _rand_bits(np.random.default_rng(190), (2, 4, 8))
+    q = np.concatenate([extra, c.q])[None]
+    lens = c.n.copy()
+    got = orc.decode_multi(q, c.k_cache, c.v_cache, c.table, lens, c.scale)
+    assert np.array_equal(got[0, :2], np.zeros((2, 4, 8)))
+    np.testing.assert_allclose(got[0, 2:], c.sdpa(), rtol=1e-12, atol=1e-12)
+    empty = orc.decode_multi(q, c.k_cache, c.v_cache, c.table, np.array([0], np.int32),
+                             c.scale)
+    assert np.array_equal(empty, np.zeros_like(empty))
+
+
 def _wl_np(w):
     return dict(q=inputs.bf16_bits(w.q), kc=inputs.bf16_bits(w.k_cache),
                 vc=inputs.bf16_bits(w.v_cache), table=w.page_table_np,
@@ -294,7 +328,8 @@ PINS = [pin_store_kv_is_index_assignment, pin_vs_sdpa, pin_decode_vs_sdpa,
         pin_large_scale_is_argmax, pin_brute_force_scalar,
         pin_page_permutation_invariance, pin_gqa_is_repeated_mha,
         pin_chunked_prefill_matches_full, pin_decode_is_one_row_prefill,
-        pin_golden_cu_seqlens]
+        pin_golden_cu_seqlens, pin_decode_multi_vs_sdpa,
+        pin_decode_multi_one_token_is_decode, pin_decode_multi_short_context]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
