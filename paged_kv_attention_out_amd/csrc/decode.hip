@@ -73,7 +73,8 @@ struct DecodeParams {
   int32_t split;
   int32_t n_split_max;
   int32_t q_len;     // query tokens per request (1 for plain decode)
-  int32_t q_slices;  // blocks per (request, KV head, split): each takes LQ query tokens
+  int32_t q_slices;  // units per (request, KV head, split): each takes LQ query tokens
+  int32_t heads_per_block;  // waves per workgroup, one per KV head (1 or 2)
   float scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -139,7 +140,7 @@ struct DecodeTraits {
 //   O (16 head rows x D dims) lives in D/16 accumulators of 4 registers;
 //   row 4c+i is query head i % G.
 template <int D, int G, int LQ>
-__global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(128, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
   constexpr int KCH = D / 32;  // 16-byte pieces per lane per row == QK MFMAs per group
   constexpr int NT = D / 16;   // 16-dim tiles of the output == PV MFMAs per pair
   constexpr int NBUF = DecodeTraits<D, G>::NBUF;
@@ -147,9 +148,15 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   constexpr int NC = G * LQ;     // distinct query columns: (query token, query head)
   static_assert(G == 1 || G == 2 || G == 4, "query heads per KV head");
   static_assert(NC <= 16 && (16 % NC) == 0, "the 16 MFMA columns hold whole copies of the columns");
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[NBUF * 16 * VPITCH];
+  // LDS: NBUF * 16 * VPITCH values per wave, sized at launch.
+  extern __shared__ __attribute__((aligned(16))) uint16_t vlds_block[];
+  // A workgroup holds heads_per_block waves, one per KV head of the same
+  // unit: adjacent heads' slices of every token row are then read by one
+  // CU at the same time.
+  const int wv = (int)(threadIdx.x >> 6);
+  uint16_t* vlds = vlds_block + wv * (NBUF * 16 * VPITCH);
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   // Block -> unit: rank = block / (Hkv * slices) walks the (request, split) pairs that
   // exist -- request-major, each request with max(ceil(n / split), 1)
   // splits -- so every block of the grid past the last pair sits at its end
@@ -158,17 +165,15 @@ __global__ __launch_bounds__(64, 2) PKV_DECODE_OCC void decode_split_kernel(Deco
   // It rotates from one rank to the next because blocks land on the 8 XCDs
   // round-robin: every XCD then sees every head's offset within the page rows.
   // With several query slices (multi-token queries wider than the 16 MFMA
-  // columns) the slices of one unit are Hkv blocks apart: with Hkv a
-  // multiple of 8 they share an XCD, so the second slice reads K/V from L2.
-  const uint32_t u = blockIdx.x / (uint32_t)p.num_kv_heads;
+  // columns) the slices of one unit are Hkv / heads_per_block blocks apart:
+  // with that a multiple of 8 they share an XCD, so the second slice reads
+  // K/V from L2.
+  const uint32_t hblocks = (uint32_t)(p.num_kv_heads / p.heads_per_block);  // blocks per unit
+  const uint32_t u = blockIdx.x / hblocks;
   const uint32_t rank = LQ == 1 ? u : u / (uint32_t)p.q_slices;
   const int tq0 = LQ == 1 ? 0 : (int)(u % (uint32_t)p.q_slices) * LQ;  // first query token
   const int QL = LQ == 1 ? 1 : p.q_len;
-#ifdef PKV_DECODE_NO_ROTATE
-  const int kvh = (int)(blockIdx.x % (uint32_t)p.num_kv_heads);
-#else
-  const int kvh = (int)((blockIdx.x + rank) % (uint32_t)p.num_kv_heads);
-#endif
+  const int kvh = (int)((blockIdx.x + rank) % hblocks) * p.heads_per_block + wv;
   int r = -1, split = 0, n = 0;
   {
     int base = 0;  // pairs of the requests before this chunk of 64
@@ -642,8 +647,10 @@ bool decode_shape_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
 
 template <int D, int G, int LQ>
 int launch_decode(const DecodeParams& p, int64_t blocks, hipStream_t s) {
+  constexpr size_t kWaveLds = (size_t)DecodeTraits<D, G>::NBUF * 16 * (D + 8) * sizeof(uint16_t);
   const int st = pkv_host::launch(decode_split_kernel<D, G, LQ>, dim3((unsigned)blocks),
-                                  dim3(64), s, p);
+                                  dim3(64 * p.heads_per_block), s, p,
+                                  kWaveLds * p.heads_per_block);
   if (st != PKV_OK || p.n_split_max <= 1) return st;
   const int64_t cblocks = ((int64_t)p.num_seqs * p.q_len * p.num_q_heads + 3) / 4;
   return pkv_host::launch(decode_combine_kernel<D, G>, dim3((unsigned)cblocks), dim3(256), s,
@@ -750,9 +757,11 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
     p.ws_l = reinterpret_cast<float*>(ws + w.l);
     p.ws_o = reinterpret_cast<float*>(ws + w.o);
   }
-  // One block per (request, split) pair, KV head and query slice, at most
-  // this many; blocks past the pairs that exist exit at once.
-  const int64_t blocks = rk * nsm * slices;
+  // One wave per (request, split) pair, KV head and query slice, two KV
+  // heads per workgroup when Hkv is even; at most this many workgroups,
+  // those past the pairs that exist exit at once.
+  const int hpb = num_kv_heads % 2 == 0 ? 2 : 1;
+  const int64_t blocks = rk * nsm * slices / hpb;
   if (blocks > INT32_MAX) return PKV_EINVAL;
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -780,6 +789,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   p.n_split_max = (int32_t)nsm;
   p.q_len = q_len;
   p.q_slices = slices;
+  p.heads_per_block = hpb;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (head_dim == 64) {

@@ -72,10 +72,11 @@ inline bool finite_positive(float x) { return x > 0.0f && x <= 3.4028234e38f; }
 // Launch a kernel whose only argument is a parameter struct; the status
 // reported is this launch's own (hipLaunchKernel's return value).
 template <typename P>
-inline int launch(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t stream, P params) {
+inline int launch(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t stream, P params,
+                  size_t dynamic_lds = 0) {
   void* args[] = {&params};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0,
-                                 stream);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args,
+                                 dynamic_lds, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
