@@ -7,8 +7,9 @@
 //
 // Two kernels on the caller's stream:
 //
-// decode_split_kernel -- one wavefront per (request r, KV head kvh, split s).
-//   A split is `split` consecutive tokens; a request with n tokens has
+// decode_split_kernel -- one wavefront per (request r, KV head kvh, split s),
+//   two of them (adjacent KV heads of one split) per workgroup when Hkv is
+//   even.  A split is `split` consecutive tokens; a request with n tokens has
 //   ceil(n/split) splits.  The wave walks its tokens 16 at a time ("groups"):
 //   * S^T = K Q^T on MFMA 16x16x32 bf16: each lane's K loads (8 dims of its
 //     token's row per 32-dim block) are the A operand as loaded; the B
