@@ -167,13 +167,6 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = ld16(qp + 16 * ks);
       if (!valid) v = make_uint4(0, 0, 0, 0);
-      // Q pre-scaled by softmax_scale * log2(e) (rounded to bf16): the QK
-      // product is then the base-2 exponent itself.
-      const float cs = p.scale_log2;
-      v.x = pack_bf16x2(bf16_lo(v.x) * cs, bf16_hi(v.x) * cs);
-      v.y = pack_bf16x2(bf16_lo(v.y) * cs, bf16_hi(v.y) * cs);
-      v.z = pack_bf16x2(bf16_lo(v.z) * cs, bf16_hi(v.z) * cs);
-      v.w = pack_bf16x2(bf16_lo(v.w) * cs, bf16_hi(v.w) * cs);
       qb[nb][ks] = as_bf16x8(v);
     }
   }
@@ -223,24 +216,18 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
     }
   };
 
-  // Softmax reference point m of each column, kept exactly representable in
-  // bf16: one more MFMA k-block per score tile, A = 1 in k-slot 0 for every
-  // key and B = -m in k-slot 0 for every column, adds -m to the scores, so
-  // the exponent needs no per-score arithmetic.
   f32x16 oacc[DB][NB];
-  float m[NB], l[NB][4];  // row sums in 4 independent partial chains
-  bf16x8 qm[NB];
-  const bf16x8 a_one = as_bf16x8(make_uint4(half == 0 ? 0x3f80u : 0u, 0u, 0u, 0u));
+  float m[NB], l[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    m[nb] = 0.f;
-    qm[nb] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
-    l[nb][0] = l[nb][1] = l[nb][2] = l[nb][3] = 0.f;
+    m[nb] = kNegInf;
+    l[nb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int v = 0; v < 16; ++v) oacc[db][nb][v] = 0.f;
   }
+  const float c = p.scale_log2;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
   // Offsets of this lane's operand reads inside one tile (elements).
@@ -267,16 +254,14 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
     const uint16_t* Kt = kv[kt & 1][0];
     const uint16_t* Vt = kv[kt & 1][1];
 
-    // S^T tile: rows = 64 keys (two 32-key halves), columns = this wave's;
-    // entries are s * scale * log2(e) - m.
+    // S^T tile: rows = 64 keys (two 32-key halves), columns = this wave's.
     f32x16 sacc[NB][2];
-    const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                           0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
-        sacc[nb][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_one, qm[nb], zero16, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[nb][kh][v] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -306,10 +291,8 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
       }
     }
 
-    // Column maxima relative to m; lazy rescale: m moves up only when a
-    // score exceeds it by more than kTau (on an item's first tile it is set
-    // to that tile's maximum).
-    bool grow = kt == 0;
+    // Column maxima of the raw scores (the scale is positive), lazy rescale.
+    bool grow = false;
     float mt[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -320,30 +303,20 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
         a = fmaxf(a, fmaxf(sacc[nb][0][v], sacc[nb][1][v]));
         b = fmaxf(b, fmaxf(sacc[nb][0][v + 1], sacc[nb][1][v + 1]));
       }
-      mt[nb] = max_xor32(fmaxf(a, b));
-      grow |= mt[nb] > kTau;
+      mt[nb] = max_xor32(fmaxf(a, b)) * c;
+      grow |= mt[nb] > m[nb] + kTau;
     }
     if (__any(grow)) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        // new m = m + mt rounded to bf16; dl = the shift (0 for a column
-        // that keeps its m, e.g. one whose keys here are all masked)
-        const bool g = (kt == 0 || mt[nb] > kTau) && mt[nb] != kNegInf;
-        const float mn = g ? bf16_lo(to_bf16(m[nb] + mt[nb])) : m[nb];
-        const float dl = mn - m[nb];
-        const float al = kt == 0 ? 0.f : fast_exp2(-dl);  // nothing accumulated before tile 0
-#pragma unroll
-        for (int j = 0; j < 4; ++j) l[nb][j] *= al;
+        const float mn = fmaxf(m[nb], mt[nb]);
+        const float al = mn == kNegInf ? 1.f : fast_exp2(m[nb] - mn);
+        l[nb] *= al;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int v = 0; v < 16; ++v) oacc[db][nb][v] *= al;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sacc[nb][kh][v] -= dl;
         m[nb] = mn;
-        qm[nb] = as_bf16x8(make_uint4(half == 0 ? (uint32_t)to_bf16(-mn) : 0u, 0u, 0u, 0u));
       }
     }
 
@@ -358,13 +331,14 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
         bf16x8 pb[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+          const float nm = -m[nb];
           uint32_t w[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float e0 = fast_exp2(sacc[nb][kh][8 * u + 2 * j]);
-            const float e1 = fast_exp2(sacc[nb][kh][8 * u + 2 * j + 1]);
+            const float e0 = fast_exp2(__builtin_fmaf(sacc[nb][kh][8 * u + 2 * j], c, nm));
+            const float e1 = fast_exp2(__builtin_fmaf(sacc[nb][kh][8 * u + 2 * j + 1], c, nm));
             w[j] = pack_bf16x2(e0, e1);
-            l[nb][j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, l[nb][j],
+            l[nb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, l[nb],
                                                     false);
           }
           pb[nb] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
@@ -387,8 +361,7 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
   // db*32 + 8*(v/4) + 4*half + v%4 of its column.
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float ls = (l[nb][0] + l[nb][1]) + (l[nb][2] + l[nb][3]);
-    const float lt = ls + __shfl_xor(ls, 32);
+    const float lt = l[nb] + __shfl_xor(l[nb], 32);
     if (pos[nb] > qlast) continue;
     const float inv = 1.f / lt;
     uint16_t* op = p.out + ((int64_t)(s0 + pos[nb]) * p.num_q_heads + kvh * G + hb[nb]) * D;

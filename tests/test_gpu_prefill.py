@@ -128,3 +128,39 @@ def test_prefill_workspace_returns_to_zero():
         torch.cuda.synchronize()
         assert int(ws.count_nonzero()) == 0, f"call {i} left the counter non-zero"
         assert_close(f64(out), ref, f"workspace call {i}")
+
+
+def _shifted(w, q_add=0.0, k_add=0.0, k_outlier_frac=0.0, scale=None, seed=0):
+    """Host workload with shifted q / K values (NaN poison stays NaN) and
+    optionally a fraction of K rows (pool and new rows) scaled by 8."""
+    g = torch.Generator().manual_seed(seed)
+    w.q = (w.q.float() + q_add).to(torch.bfloat16)
+    for name in ("k_cache", "k_new"):
+        t = getattr(w, name).float() + k_add
+        if k_outlier_frac:
+            rows = t.view(-1, t.shape[-1])
+            pick = torch.rand(rows.shape[0], generator=g) < k_outlier_frac
+            rows[pick] *= 8.0
+        setattr(w, name, t.to(torch.bfloat16))
+    if scale is not None:
+        w.scale = scale
+    return w.to("cuda")
+
+
+@pytest.mark.parametrize("kind", ["large_scale_outliers", "all_scores_negative"])
+def test_prefill_extreme_scores(kind):
+    # The kernel keeps each column's softmax reference point in bf16 and
+    # moves it only when a tile's maximum exceeds it by more than 8: large
+    # scores (coarse bf16 spacing of the reference, frequent moves) and
+    # uniformly very negative scores (reference far below 0) both exercise it.
+    w = inputs.build_prefill(3, 8, 2, 64, 16, [200, 0, 37], [150, 300, 64], seed=61)
+    if kind == "large_scale_outliers":
+        w = _shifted(w, k_outlier_frac=0.02, scale=1.0, seed=62)
+    else:
+        w = _shifted(w, q_add=3.0, k_add=-3.0)
+    print(f"prefill extreme scores: {kind}", flush=True)
+    ref = _oracle(w)
+    run_store(w)
+    out = run_prefill(w)
+    torch.cuda.synchronize()
+    print(kind, assert_close(f64(out), ref, kind))
