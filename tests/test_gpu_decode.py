@@ -236,3 +236,52 @@ def test_shared_prefix_decode_workload():
                               w.page_table, w.seq_lens, w.max_seq_len, w.scale)
     torch.cuda.synchronize()
     print("shared prefix max/mean err", assert_close(f64(out), ref, "shared prefix"))
+
+
+def _shift_decode(w, q_add=0.0, k_add=0.0, k_outlier_frac=0.0, scale=None, seed=0):
+    """Host decode workload with shifted q / K values (NaN poison stays NaN),
+    optionally a fraction of K rows scaled by 8, and another softmax scale."""
+    g = torch.Generator().manual_seed(seed)
+    w.q = (w.q.float() + q_add).to(torch.bfloat16)
+    for name in ("k_cache", "k_new"):
+        t = getattr(w, name)
+        if t is None:
+            continue
+        t = t.float() + k_add
+        if k_outlier_frac:
+            rows = t.view(-1, t.shape[-1])
+            pick = torch.rand(rows.shape[0], generator=g) < k_outlier_frac
+            rows[pick] *= 8.0
+        setattr(w, name, t.to(torch.bfloat16))
+    if scale is not None:
+        w.scale = scale
+    return w.to("cuda")
+
+
+@pytest.mark.parametrize("kind", ["large_scale_outliers", "all_scores_negative"])
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_decode_extreme_scores(kind, q_len):
+    # Large scores (softmax_scale 1.0 with x8 key outliers: a near one-hot
+    # softmax, frequent moves of the running max) and uniformly very negative
+    # scores, through the split path (several splits per request + merge).
+    lens = [37, 700, 1500]
+    w = inputs.build_decode(3, 16, 4, 64, 16, lens, seed=71 + q_len, q_len=q_len,
+                            store_new=q_len == 1)
+    if kind == "large_scale_outliers":
+        w = _shift_decode(w, k_outlier_frac=0.02, scale=1.0, seed=72)
+    else:
+        w = _shift_decode(w, q_add=3.0, k_add=-3.0)
+    print(f"decode extreme scores: {kind} q_len={q_len}", flush=True)
+    kc, vc = host_pools(w)
+    if q_len == 1:
+        ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale)
+        run_store(w)
+        out = run_decode(w, split_tokens=128)
+    else:
+        ref = orc.decode_multi(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np,
+                               w.scale)
+        out = pkv.pkv_paged_attn_decode_multi(w.q, w.k_cache, w.v_cache, w.page_table,
+                                              w.seq_lens, w.max_seq_len, w.scale,
+                                              split_tokens=128)
+    torch.cuda.synchronize()
+    print(kind, q_len, assert_close(f64(out), ref, kind))
