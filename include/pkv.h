@@ -97,9 +97,13 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t max_seq_len, int32_t split_tokens);
 
 /*
- * pkv_decode_split_tokens -- the split length (tokens per split) that
- * pkv_paged_attn_decode uses for these arguments; split_tokens != 0 is
- * returned rounded as the call would use it.  0 on invalid arguments.
+ * pkv_decode_split_tokens -- the split length (tokens per split) the host
+ * picks for these arguments, which sizes the launch and the workspace;
+ * split_tokens != 0 is returned as the call would use it.  With
+ * split_tokens = 0 and a batch that needs only a few rounds of the GPU's
+ * resident wavefronts (at most 256 requests), the call may use a longer
+ * split chosen on the device from the actual lengths, so that all work
+ * units fit one round.  0 on invalid arguments.
  */
 int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                 int32_t max_seq_len, int32_t split_tokens);
@@ -133,7 +137,8 @@ int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *   page_size    : 16, 32, 64, 128 or 256
  *   num_q_heads / num_kv_heads : 1, 2 or 4
  *   softmax_scale: finite and > 0 (typically 1/sqrt(head_dim))
- *   split_tokens : 0 = automatic, else a multiple of 16 in [16, 65536]
+ *   split_tokens : 0 = automatic (see pkv_decode_split_tokens), else a
+ *                  multiple of 16 in [16, 65536]
  *   out          : [num_seqs, num_q_heads, head_dim] bf16 (round to nearest even)
  *   workspace    : device scratch of at least pkv_decode_workspace_bytes(...)
  *                  bytes, 256-byte aligned, for the per-split partial results

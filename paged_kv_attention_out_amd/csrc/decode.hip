@@ -31,6 +31,9 @@
 // Bandwidth: every K/V byte of the context is read once; partials add
 // splits * g * (D + 2) * 4 bytes written and read per (r, kvh).
 
+#include <algorithm>
+#include <atomic>
+
 #include "pkv_common.h"
 
 #ifndef PKV_DECODE_NBUF_D64
@@ -63,6 +66,7 @@ struct DecodeParams {
   float* ws_m;  // [B * Hkv * n_split_max * g]
   float* ws_l;
   float* ws_o;  // [B * Hkv * n_split_max * g * D]
+  int32_t* ws_split;  // the split the split kernel used (read by the combine)
   int64_t num_pages;
   int32_t page_size;
   int32_t page_shift;
@@ -71,8 +75,10 @@ struct DecodeParams {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_seq_len;
-  int32_t split;
-  int32_t n_split_max;
+  int32_t split;        // host split (tokens); the device may pick a longer one
+  int32_t n_split_max;  // splits per request at the host split (sizes grid and workspace)
+  int32_t round_units;  // units per KV head and query slice that one round of resident
+                        // waves holds; 0 = use `split` as given
   int32_t q_len;     // query tokens per request (1 for plain decode)
   int32_t q_slices;  // units per (request, KV head, split): each takes LQ query tokens
   int32_t heads_per_block;  // waves per workgroup, one per KV head (1 or 2)
@@ -107,6 +113,87 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<kHalfMirror>(v);
   v += dpp<kRowMirror>(v);
   return v;
+}
+
+// Sum over the wavefront: DPP sums inside each row of 16 lanes, then the
+// four row totals read as scalars (no LDS permutes).
+__device__ __forceinline__ int wave_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);  // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// Split length of a call whose split is chosen on the device.  Work units
+// are (request, split) pairs, and the call time follows how they fill
+// rounds of the waves that are resident at once: for a batch that needs few
+// rounds, a split just long enough that all units fit one round beats a
+// shorter split that leaves a partial last round (measured on the
+// Llama-shaped, shared-prefix and speculative batches).  The host enables
+// this (round_units > 0) only for batches of at most 256 requests that need
+// at most 4 rounds at its split even at the longest length, and then
+// launches one round of workgroups.  The split kernel takes a multiple of 16
+// at or above the host split whose units fit that round (always possible:
+// every request is one unit at split >= its length, and num_seqs <=
+// round_units): the estimate from units(s) ~ tokens/s + num_seqs/2 when its
+// exact count fits, else the smallest fitting one above it.
+__device__ int device_split(const DecodeParams& p) {
+  const int T = p.round_units;
+  if (T <= 0) return p.split;
+  const int lane = (int)(threadIdx.x & 63);
+  int len[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rr = 64 * k + lane;
+    len[k] = rr < p.num_seqs ? min(p.seq_lens[rr], p.max_seq_len) : -1;  // -1: no request
+  }
+  const int nk = (p.num_seqs + 63) >> 6;  // chunks of 64 requests that exist
+  auto units = [&](int x) {  // max(ceil(n / x), 1) per request, summed (exact)
+    const float inv = 1.f / (float)x;
+    int u = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < nk && len[k] >= 0) {
+        // ceil(n / x) from a float quotient corrected by integer products
+        int q = (int)((float)len[k] * inv);
+        q += q * x < len[k];
+        q += q * x < len[k];
+        q -= q > 0 && (q - 1) * x >= len[k];
+        u += max(q, 1);
+      }
+    }
+    return wave_sum(u);
+  };
+  // (the host's gate keeps tokens <= 4 * T * split, far below 2^31)
+  int tokens = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) tokens += max(len[k], 0);
+  tokens = wave_sum(tokens);
+  const int denom = max(T - p.num_seqs / 2, 1);
+  const int est = max(p.split, ((tokens + denom - 1) / denom + 15) & ~15);
+  // Otherwise gallop up from the estimate to a bracket (bad, good] --
+  // units(bad) > T >= units(good) -- and bisect it; units() does not increase
+  // with the split, and at split >= the longest request it is num_seqs <= T,
+  // so the gallop ends.
+  int good, bad, step = 16;
+  if (units(est) <= T) {
+    return est;
+  } else {
+    bad = est;
+    good = est + step;
+    while (units(good) > T) {
+      bad = good;
+      step *= 2;
+      good = bad + step;
+    }
+  }
+  while (good - bad > 16) {
+    const int mid = bad + (((good - bad) >> 1) & ~15);
+    if (units(mid) <= T) good = mid; else bad = mid;
+  }
+  return good;
 }
 
 #ifdef PKV_DECODE_WAVES_PER_EU
@@ -175,6 +262,8 @@ __global__ __launch_bounds__(128, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   const int tq0 = LQ == 1 ? 0 : (int)(u % (uint32_t)p.q_slices) * LQ;  // first query token
   const int QL = LQ == 1 ? 1 : p.q_len;
   const int kvh = (int)((blockIdx.x + rank) % hblocks) * p.heads_per_block + wv;
+  const int sl = device_split(p);  // tokens per split
+  if (p.ws_split != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *p.ws_split = sl;
   int r = -1, split = 0, n = 0;
   {
     int base = 0;  // pairs of the requests before this chunk of 64
@@ -183,7 +272,7 @@ __global__ __launch_bounds__(128, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
       int len = 0, cnt = 0;
       if (rr < p.num_seqs) {
         len = min(p.seq_lens[rr], p.max_seq_len);
-        cnt = len <= 0 ? 1 : (len + p.split - 1) / p.split;
+        cnt = len <= 0 ? 1 : (len + sl - 1) / sl;
       }
       int inc = cnt;  // inclusive scan over the lanes
 #pragma unroll
@@ -213,7 +302,7 @@ __global__ __launch_bounds__(128, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   // Query token of the column; columns past the last token repeat it and
   // are never written.
   const int tq = min(tq0 + col / G, QL - 1);
-  const int t_begin = split * p.split;
+  const int t_begin = split * sl;
 
   // Q^T fragments (B operand): column j holds query token tq of head
   // kvh*G + hcol (the NC columns repeat over the 16 MFMA columns).
@@ -251,8 +340,8 @@ __global__ __launch_bounds__(128, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
     }
     return;
   }
-  const int ns = (n + p.split - 1) / p.split;
-  const int t_end = min(n, t_begin + p.split);
+  const int ns = (n + sl - 1) / sl;
+  const int t_end = min(n, t_begin + sl);
 
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
   // Fused step: the request's last split writes this head's slice of the
@@ -527,19 +616,24 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const float* oo = p.ws_o + (sbase * NC + x) * D + lane;
 
   int n = p.seq_lens[r];
-  // First batch of partials, issued together with the length.
+  // First batch of partials, issued together with the length.  With a
+  // device-chosen split the units fit one round, so requests have few
+  // splits: only 8 are fetched ahead (the bound nsm, from the host split,
+  // can be far above the real count), the rest once the count is known.
+  const int pre = min(nsm, p.round_units > 0 ? 8 : kCombineBatch);
   float mv = lane < nsm ? om[(int64_t)lane * NC] : kNegInf;
   float lv = lane < nsm ? ol[(int64_t)lane * NC] : 0.f;
   float v[kCombineBatch][DPL];
 #pragma unroll
   for (int k = 0; k < kCombineBatch; ++k)
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) v[k][i] = k < nsm ? oo[(int64_t)k * NC * D + 64 * i] : 0.f;
+    for (int i = 0; i < DPL; ++i) v[k][i] = k < pre ? oo[(int64_t)k * NC * D + 64 * i] : 0.f;
 
   n = uniform(n);
   n = n > p.max_seq_len ? p.max_seq_len : n;
   if (n <= 0) return;
-  const int ns = (n + p.split - 1) / p.split;
+  const int sl = p.round_units > 0 ? uniform(*p.ws_split) : p.split;  // as the split kernel used
+  const int ns = (n + sl - 1) / sl;
   if (ns == 1) return;  // written by the split kernel
 
   // Global max over the splits (lane s holds split s, 64 at a time).
@@ -566,7 +660,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     // lane = output dim; the weights of the 64 splits are broadcast by readlane
     const int cnt = min(64, ns - s0);
     for (int k0 = 0; k0 < cnt; k0 += kCombineBatch) {
-      if (s0 + k0 != 0) {  // later batches: load now (the first came with the length)
+      // later batches load now; the first came with the length, unless it
+      // holds more splits than were fetched ahead (then it is read again)
+      if (s0 + k0 != 0 || min(cnt, kCombineBatch) > pre) {
 #pragma unroll
         for (int k = 0; k < kCombineBatch; ++k)
 #pragma unroll
@@ -610,7 +706,7 @@ int32_t choose_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct WsLayout {
-  size_t m, l, o, total;
+  size_t m, l, o, split, total;
 };
 
 // ncols = query columns per (request, KV head): g * q_len
@@ -619,7 +715,8 @@ WsLayout ws_layout(int64_t rk, int64_t nsm, int64_t ncols, int d) {
   w.m = 0;
   w.l = w.m + align256(rk * nsm * ncols * sizeof(float));
   w.o = w.l + align256(rk * nsm * ncols * sizeof(float));
-  w.total = w.o + align256(rk * nsm * ncols * d * sizeof(float));
+  w.split = w.o + align256(rk * nsm * ncols * d * sizeof(float));
+  w.total = w.split + 256;
   return w;
 }
 
@@ -646,9 +743,50 @@ bool decode_shape_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
   return true;
 }
 
+// Waves of decode_split_kernel<D, G, LQ> resident on the current device at
+// once with hpb waves per workgroup (occupancy x CUs, cached per device).
 template <int D, int G, int LQ>
-int launch_decode(const DecodeParams& p, int64_t blocks, hipStream_t s) {
+int resident_waves(int hpb) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices][2];
   constexpr size_t kWaveLds = (size_t)DecodeTraits<D, G>::NBUF * 16 * (D + 8) * sizeof(uint16_t);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  const int slot = hpb == 2 ? 1 : 0;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev][slot].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(decode_split_kernel<D, G, LQ>), 64 * hpb,
+          kWaveLds * hpb) != hipSuccess)
+    return 0;
+  const int n = cus * per_cu * hpb;
+  if (n > 0 && dev < kMaxDevices) cache[dev][slot].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int D, int G, int LQ>
+int launch_decode(DecodeParams p, int64_t blocks, hipStream_t s) {
+  constexpr size_t kWaveLds = (size_t)DecodeTraits<D, G>::NBUF * 16 * (D + 8) * sizeof(uint16_t);
+  if (p.round_units < 0) {
+    // Units per KV head and query slice that one round of resident waves
+    // holds.  Use the device's split choice only when even max-length
+    // requests need at most 4 rounds at the host split; then one round of
+    // workgroups covers every unit it can produce.
+    const int64_t per_unit = (int64_t)p.num_kv_heads * (LQ == 1 ? 1 : p.q_slices);
+    const int64_t T = resident_waves<D, G, LQ>(p.heads_per_block) / per_unit;
+    const int64_t worst = (int64_t)p.num_seqs * p.n_split_max;  // units per head at the host split
+    if (T > 0 && p.num_seqs <= T && worst <= 4 * T) {
+      p.round_units = (int32_t)T;
+      blocks = std::min<int64_t>(blocks, T * per_unit / p.heads_per_block);
+    } else {
+      p.round_units = 0;
+    }
+  }
   const int st = pkv_host::launch(decode_split_kernel<D, G, LQ>, dim3((unsigned)blocks),
                                   dim3(64 * p.heads_per_block), s, p,
                                   kWaveLds * p.heads_per_block);
@@ -757,6 +895,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
     p.ws_m = reinterpret_cast<float*>(ws + w.m);
     p.ws_l = reinterpret_cast<float*>(ws + w.l);
     p.ws_o = reinterpret_cast<float*>(ws + w.o);
+    p.ws_split = reinterpret_cast<int32_t*>(ws + w.split);
   }
   // One wave per (request, split) pair, KV head and query slice, two KV
   // heads per workgroup when Hkv is even; at most this many workgroups,
@@ -788,6 +927,9 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   p.max_seq_len = max_seq_len;
   p.split = split;
   p.n_split_max = (int32_t)nsm;
+  // Device-chosen split (see device_split): only for the automatic split and
+  // batches that need few rounds even at the longest length.
+  p.round_units = split_tokens == 0 && num_seqs <= 256 ? -1 : 0;
   p.q_len = q_len;
   p.q_slices = slices;
   p.heads_per_block = hpb;
