@@ -285,3 +285,50 @@ def test_decode_extreme_scores(kind, q_len):
                                               split_tokens=128)
     torch.cuda.synchronize()
     print(kind, q_len, assert_close(f64(out), ref, kind))
+
+
+@pytest.mark.parametrize("B,lo,hi,q_len", [
+    (250, 50, 300, 1),     # the device's split choice reads four chunks of 64 lengths
+    (100, 100, 600, 1),
+    (100, 100, 600, 2),
+])
+def test_decode_device_chosen_split(B, lo, hi, q_len):
+    # With the automatic split, batches that need few rounds of resident
+    # waves get a split chosen on the device from the actual lengths (here
+    # longer than the host's); the merge reads the split the split kernel
+    # recorded.  Parity against the oracle on every element.
+    rng = np.random.default_rng(B + hi + q_len)
+    lens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+    lens[3] = 0   # an empty request among them
+    w = inputs.build_decode(B, 32, 8, 64, 16, lens, seed=int(B + q_len), device="cuda",
+                            q_len=q_len)
+    kc, vc = host_pools(w)
+    print(f"device-chosen split: B={B} lens {lo}..{hi} q_len={q_len} host split "
+          f"{pkv.pkv_decode_split_tokens(B, 8, w.max_seq_len)}", flush=True)
+    if q_len == 1:
+        ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale,
+                         requests=[r for r in range(B) if lens[r] > 0])
+        out = run_decode(w)
+    else:
+        ref = orc.decode_multi(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np,
+                               w.scale)
+        out = pkv.pkv_paged_attn_decode_multi(w.q, w.k_cache, w.v_cache, w.page_table,
+                                              w.seq_lens, w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    got = f64(out)
+    assert np.array_equal(got[3], np.zeros_like(got[3]))
+    ref[3] = 0.0
+    assert_close(got, ref, f"B{B}")
+
+
+def test_decode_merge_of_many_splits():
+    # A few long requests with more splits than the merge fetches ahead.
+    lens = np.array([100, 5000, 40, 3000], np.int32)
+    w = inputs.build_decode(4, 32, 8, 64, 16, lens, seed=83, device="cuda", store_new=True)
+    kc, vc = host_pools(w)
+    ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale)
+    print(f"many splits: host split {pkv.pkv_decode_split_tokens(4, 8, w.max_seq_len)}", flush=True)
+    run_store(w)
+    out = run_decode(w)
+    torch.cuda.synchronize()
+    assert_close(f64(out), ref, "many splits")
