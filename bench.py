@@ -245,6 +245,10 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
             raise RuntimeError(f"{name}: non-finite output")
     if R > 1 and not torch.equal(calls[0][2], calls[1][2]):
         raise RuntimeError(f"{name}: replicas disagree")
+    # the split the kernels used: recorded by the split kernel in the last
+    # 256-byte slot of the decode workspace (the device may pick a longer one)
+    if is_decode and ws is not None:
+        split = int(ws[-256:].view(torch.int32)[0].item())
     res = dict(workload=w, replicas=R, split=split, fused=fused,
                ms_per_step=(t1 - t0) * 1e3 / steps,
                kernel_ms_mean=float(np.mean(kernel_ms)), kernel_ms_median=float(np.median(kernel_ms)),
