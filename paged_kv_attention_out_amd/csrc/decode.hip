@@ -81,7 +81,7 @@ struct DecodeParams {
                         // waves holds; 0 = use `split` as given
   int32_t q_len;     // query tokens per request (1 for plain decode)
   int32_t q_slices;  // units per (request, KV head, split): each takes LQ query tokens
-  int32_t heads_per_block;  // waves per workgroup, one per KV head (1 or 2)
+  int32_t heads_per_block;  // waves per workgroup, one per KV head (1, 2, 4 or 8)
   float scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -228,7 +228,7 @@ struct DecodeTraits {
 //   O (16 head rows x D dims) lives in D/16 accumulators of 4 registers;
 //   row 4c+i is query head i % G.
 template <int D, int G, int LQ>
-__global__ __launch_bounds__(128, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
   constexpr int KCH = D / 32;  // 16-byte pieces per lane per row == QK MFMAs per group
   constexpr int NT = D / 16;   // 16-dim tiles of the output == PV MFMAs per pair
   constexpr int NBUF = DecodeTraits<D, G>::NBUF;
@@ -748,11 +748,11 @@ bool decode_shape_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
 template <int D, int G, int LQ>
 int resident_waves(int hpb) {
   constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices][2];
+  static std::atomic<int> cache[kMaxDevices][4];  // by log2(hpb)
   constexpr size_t kWaveLds = (size_t)DecodeTraits<D, G>::NBUF * 16 * (D + 8) * sizeof(uint16_t);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  const int slot = hpb == 2 ? 1 : 0;
+  const int slot = hpb >= 8 ? 3 : hpb >= 4 ? 2 : hpb - 1;
   if (dev < kMaxDevices) {
     const int c = cache[dev][slot].load(std::memory_order_relaxed);
     if (c > 0) return c;
@@ -770,23 +770,35 @@ int resident_waves(int hpb) {
 }
 
 template <int D, int G, int LQ>
-int launch_decode(DecodeParams p, int64_t blocks, hipStream_t s) {
+int launch_decode(DecodeParams p, int64_t waves, hipStream_t s) {
   constexpr size_t kWaveLds = (size_t)DecodeTraits<D, G>::NBUF * 16 * (D + 8) * sizeof(uint16_t);
+  // KV heads per workgroup: adjacent heads' slices of every token row are
+  // read by one CU at the same time.  Four when Hkv allows; eight when one
+  // round of workgroups covers every unit (no workgroup then waits for a
+  // CU, so none is held back by a slow wave of a large workgroup), while
+  // with several rounds eight per workgroup is slower than four.
+  const int hkv = p.num_kv_heads;
+  int hpb = hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1;
+  int64_t blocks = waves / hpb;
   if (p.round_units < 0) {
     // Units per KV head and query slice that one round of resident waves
     // holds.  Use the device's split choice only when even max-length
     // requests need at most 4 rounds at the host split; then one round of
     // workgroups covers every unit it can produce.
-    const int64_t per_unit = (int64_t)p.num_kv_heads * (LQ == 1 ? 1 : p.q_slices);
-    const int64_t T = resident_waves<D, G, LQ>(p.heads_per_block) / per_unit;
+    const int hpb1 = hkv % 8 == 0 ? 8 : hpb;
+    const int64_t per_unit = (int64_t)hkv * (LQ == 1 ? 1 : p.q_slices);
+    const int64_t T = resident_waves<D, G, LQ>(hpb1) / per_unit;
     const int64_t worst = (int64_t)p.num_seqs * p.n_split_max;  // units per head at the host split
     if (T > 0 && p.num_seqs <= T && worst <= 4 * T) {
       p.round_units = (int32_t)T;
-      blocks = std::min<int64_t>(blocks, T * per_unit / p.heads_per_block);
+      hpb = hpb1;
+      blocks = std::min<int64_t>(waves / hpb, T * per_unit / hpb);
     } else {
       p.round_units = 0;
     }
   }
+  if (blocks > INT32_MAX) return PKV_EINVAL;
+  p.heads_per_block = hpb;
   const int st = pkv_host::launch(decode_split_kernel<D, G, LQ>, dim3((unsigned)blocks),
                                   dim3(64 * p.heads_per_block), s, p,
                                   kWaveLds * p.heads_per_block);
@@ -797,16 +809,16 @@ int launch_decode(DecodeParams p, int64_t blocks, hipStream_t s) {
 }
 
 template <int D, int G>
-int launch_decode_lq(const DecodeParams& p, int lq, int64_t blocks, hipStream_t s) {
+int launch_decode_lq(const DecodeParams& p, int lq, int64_t waves, hipStream_t s) {
   switch (lq) {
-    case 1: return launch_decode<D, G, 1>(p, blocks, s);
-    case 2: return launch_decode<D, G, 2>(p, blocks, s);
-    case 4: return launch_decode<D, G, 4>(p, blocks, s);
+    case 1: return launch_decode<D, G, 1>(p, waves, s);
+    case 2: return launch_decode<D, G, 2>(p, waves, s);
+    case 4: return launch_decode<D, G, 4>(p, waves, s);
     case 8:
-      if constexpr (G <= 2) return launch_decode<D, G, 8>(p, blocks, s);
+      if constexpr (G <= 2) return launch_decode<D, G, 8>(p, waves, s);
       break;
     case 16:
-      if constexpr (G == 1) return launch_decode<D, G, 16>(p, blocks, s);
+      if constexpr (G == 1) return launch_decode<D, G, 16>(p, waves, s);
       break;
   }
   return PKV_EUNSUPPORTED;
@@ -897,12 +909,9 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
     p.ws_o = reinterpret_cast<float*>(ws + w.o);
     p.ws_split = reinterpret_cast<int32_t*>(ws + w.split);
   }
-  // One wave per (request, split) pair, KV head and query slice, two KV
-  // heads per workgroup when Hkv is even; at most this many workgroups,
-  // those past the pairs that exist exit at once.
-  const int hpb = num_kv_heads % 2 == 0 ? 2 : 1;
-  const int64_t blocks = rk * nsm * slices / hpb;
-  if (blocks > INT32_MAX) return PKV_EINVAL;
+  // One wave per (request, split) pair, KV head and query slice: at most
+  // this many waves, those past the pairs that exist exit at once.
+  const int64_t waves = rk * nsm * slices;
   p.q = static_cast<const uint16_t*>(q);
   p.k_cache = static_cast<const uint16_t*>(k_cache);
   p.v_cache = static_cast<const uint16_t*>(v_cache);
@@ -932,17 +941,16 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   p.round_units = split_tokens == 0 && num_seqs <= 256 ? -1 : 0;
   p.q_len = q_len;
   p.q_slices = slices;
-  p.heads_per_block = hpb;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (head_dim == 64) {
-    if (g == 1) return launch_decode_lq<64, 1>(p, lq, blocks, s);
-    if (g == 2) return launch_decode_lq<64, 2>(p, lq, blocks, s);
-    return launch_decode_lq<64, 4>(p, lq, blocks, s);
+    if (g == 1) return launch_decode_lq<64, 1>(p, lq, waves, s);
+    if (g == 2) return launch_decode_lq<64, 2>(p, lq, waves, s);
+    return launch_decode_lq<64, 4>(p, lq, waves, s);
   }
-  if (g == 1) return launch_decode_lq<128, 1>(p, lq, blocks, s);
-  if (g == 2) return launch_decode_lq<128, 2>(p, lq, blocks, s);
-  return launch_decode_lq<128, 4>(p, lq, blocks, s);
+  if (g == 1) return launch_decode_lq<128, 1>(p, lq, waves, s);
+  if (g == 2) return launch_decode_lq<128, 2>(p, lq, waves, s);
+  return launch_decode_lq<128, 4>(p, lq, waves, s);
 }
 
 }  // namespace
