@@ -126,6 +126,27 @@ __device__ __forceinline__ int wave_sum(int v) {
          __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
+// Inclusive prefix sum over the 64 lanes: inside each row of 16 lanes by
+// shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row add 0),
+// then row 0's total is added to row 1 and row 2's to row 3 (row_bcast:15),
+// and the total of rows 0-1 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return v;
+}
+
+// Request lengths of the first 256 requests, 64 per chunk (lane = request
+// within the chunk), clamped to [0, max_seq_len]; -1 where there is no
+// request.
+struct Lens4 {
+  int v[4];
+};
+
 // Split length of a call whose split is chosen on the device.  Work units
 // are (request, split) pairs, and the call time follows how they fill
 // rounds of the waves that are resident at once: for a batch that needs few
@@ -139,16 +160,10 @@ __device__ __forceinline__ int wave_sum(int v) {
 // every request is one unit at split >= its length, and num_seqs <=
 // round_units): the estimate from units(s) ~ tokens/s + num_seqs/2 when its
 // exact count fits, else the smallest fitting one above it.
-__device__ int device_split(const DecodeParams& p) {
+__device__ int device_split(const DecodeParams& p, const Lens4& lens) {
   const int T = p.round_units;
   if (T <= 0) return p.split;
-  const int lane = (int)(threadIdx.x & 63);
-  int len[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int rr = 64 * k + lane;
-    len[k] = rr < p.num_seqs ? min(p.seq_lens[rr], p.max_seq_len) : -1;  // -1: no request
-  }
+  const int* len = lens.v;  // -1: no request
   const int nk = (p.num_seqs + 63) >> 6;  // chunks of 64 requests that exist
   auto units = [&](int x) {  // max(ceil(n / x), 1) per request, summed (exact)
     const float inv = 1.f / (float)x;
@@ -262,32 +277,51 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   const int tq0 = LQ == 1 ? 0 : (int)(u % (uint32_t)p.q_slices) * LQ;  // first query token
   const int QL = LQ == 1 ? 1 : p.q_len;
   const int kvh = (int)((blockIdx.x + rank) % hblocks) * p.heads_per_block + wv;
-  const int sl = device_split(p);  // tokens per split
+  // The first 256 request lengths: four loads at clamped indices, issued
+  // together (one memory round trip; the empty asm keeps the compiler from
+  // moving each load into a branch of its own).  Then, not waited for with
+  // them, one 256-byte piece of the page table per wave: the waves of an
+  // XCD together bring the rows of a small table into its L2 while the unit
+  // is being found, so the window read below hits there.
+  Lens4 lens;
+  int pf;
+  {
+    int x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = p.seq_lens[min(64 * k + lane, p.num_seqs - 1)];
+    const int64_t pt_entries = (int64_t)p.num_seqs * p.pt_stride;
+    pf = p.page_table[min(((int64_t)(blockIdx.x >> 3) * p.heads_per_block + wv) * 64 + lane,
+                          pt_entries - 1)];
+    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      lens.v[k] = 64 * k + lane < p.num_seqs ? min(max(x[k], 0), p.max_seq_len) : -1;
+  }
+  const int sl = device_split(p, lens);  // tokens per split
   if (p.ws_split != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *p.ws_split = sl;
   int r = -1, split = 0, n = 0;
   {
     int base = 0;  // pairs of the requests before this chunk of 64
     for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
-      const int rr = c0 + lane;
-      int len = 0, cnt = 0;
-      if (rr < p.num_seqs) {
-        len = min(p.seq_lens[rr], p.max_seq_len);
-        cnt = len <= 0 ? 1 : (len + sl - 1) / sl;
+      const int k = c0 >> 6;
+      int len;  // -1: no request
+      if (k < 4) {
+        len = k == 0 ? lens.v[0] : k == 1 ? lens.v[1] : k == 2 ? lens.v[2] : lens.v[3];
+      } else {
+        const int rr = c0 + lane;
+        len = rr < p.num_seqs ? min(max(p.seq_lens[rr], 0), p.max_seq_len) : -1;
       }
-      int inc = cnt;  // inclusive scan over the lanes
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(inc, off);
-        if (lane >= off) inc += t;
-      }
-      const int total = uniform(__shfl(inc, 63));
+      const int cnt = len < 0 ? 0 : len == 0 ? 1 : (len + sl - 1) / sl;
+      const int inc = wave_incl_scan(cnt);
+      const int total = __builtin_amdgcn_readlane(inc, 63);
       if ((int)rank < base + total) {
         const int rel = (int)rank - base;
         const uint64_t hit = __ballot(rel >= inc - cnt && rel < inc);
+        if (hit == 0) break;  // (cannot happen: rank lies in this chunk)
         const int lr = (int)__builtin_ctzll(hit);
         r = c0 + lr;
-        split = rel - uniform(__shfl(inc - cnt, lr));
-        n = uniform(__shfl(len, lr));
+        split = rel - __builtin_amdgcn_readlane(inc - cnt, lr);
+        n = __builtin_amdgcn_readlane(len, lr);
         break;
       }
       base += total;
@@ -327,6 +361,7 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
     ptv = (v < 0 || (int64_t)v >= p.num_pages) ? 0 : v;  // keep accesses in the pool
   };
   load_window(t_begin >> p.page_shift);
+  asm volatile("" ::"v"(pf));  // keeps the prefetch; its wait comes with the window's
 
   if (n <= 0) {
     if (split == 0) {
