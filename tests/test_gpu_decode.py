@@ -287,37 +287,54 @@ def test_decode_extreme_scores(kind, q_len):
     print(kind, q_len, assert_close(f64(out), ref, kind))
 
 
-@pytest.mark.parametrize("B,lo,hi,q_len", [
-    (250, 50, 300, 1),     # the device's split choice reads four chunks of 64 lengths
-    (100, 100, 600, 1),
-    (100, 100, 600, 2),
+@pytest.mark.parametrize("B,hq,hkv,d,lo,hi,q_len", [
+    (250, 32, 8, 64, 50, 300, 1),     # the device's split choice reads four chunks of 64 lengths
+    (100, 32, 8, 64, 100, 600, 1),
+    (100, 32, 8, 64, 100, 600, 2),
+    (100, 16, 8, 128, 50, 900, 1),    # eight KV heads per workgroup at head_dim 128
+    (65, 16, 4, 128, 300, 2000, 1),   # four per workgroup; lengths in two chunks of 64
+    (256, 8, 2, 64, 16, 400, 1),      # two per workgroup; the largest batch the device splits
+    (130, 32, 8, 64, 10, 500, 4),
 ])
-def test_decode_device_chosen_split(B, lo, hi, q_len):
+def test_decode_device_chosen_split(B, hq, hkv, d, lo, hi, q_len):
     # With the automatic split, batches that need few rounds of resident
     # waves get a split chosen on the device from the actual lengths (here
     # longer than the host's); the merge reads the split the split kernel
-    # recorded.  Parity against the oracle on every element.
-    rng = np.random.default_rng(B + hi + q_len)
+    # recorded.  An empty and a negative length are among them (both give
+    # zeros).  Parity against the oracle on every element.
+    rng = np.random.default_rng(B + hi + q_len + d)
     lens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
-    lens[3] = 0   # an empty request among them
-    w = inputs.build_decode(B, 32, 8, 64, 16, lens, seed=int(B + q_len), device="cuda",
+    lens[3] = 0
+    w = inputs.build_decode(B, hq, hkv, d, 16, lens, seed=int(B + q_len + d), device="cuda",
                             q_len=q_len)
+    w.seq_lens[5] = -7
     kc, vc = host_pools(w)
-    print(f"device-chosen split: B={B} lens {lo}..{hi} q_len={q_len} host split "
-          f"{pkv.pkv_decode_split_tokens(B, 8, w.max_seq_len)}", flush=True)
+    print(f"device-chosen split: B={B} hq{hq} hkv{hkv} d{d} lens {lo}..{hi} q_len={q_len} "
+          f"host split {pkv.pkv_decode_split_tokens(B, hkv, w.max_seq_len)}", flush=True)
+    live = [r for r in range(B) if r not in (3, 5)]
     if q_len == 1:
         ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale,
-                         requests=[r for r in range(B) if lens[r] > 0])
-        out = run_decode(w)
+                         requests=live)
+        ws = pkv.decode_workspace(B, hq, hkv, d, w.max_seq_len)
+        out = pkv.pkv_paged_attn_decode(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens,
+                                        w.max_seq_len, w.scale, workspace=ws)
     else:
         ref = orc.decode_multi(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np,
                                w.scale)
+        ws = torch.zeros(pkv.pkv_decode_multi_workspace_bytes(B, q_len, hq, hkv, d,
+                                                              w.max_seq_len),
+                         dtype=torch.uint8, device="cuda")
         out = pkv.pkv_paged_attn_decode_multi(w.q, w.k_cache, w.v_cache, w.page_table,
-                                              w.seq_lens, w.max_seq_len, w.scale)
+                                              w.seq_lens, w.max_seq_len, w.scale, workspace=ws)
     torch.cuda.synchronize()
+    # the split the kernels used is recorded in the workspace's last 256 bytes
+    used = int(ws[-256:].view(torch.int32)[0].item())
+    host = pkv.pkv_decode_split_tokens(B, hkv, w.max_seq_len)
+    assert used >= host and used % 16 == 0, (used, host)
     got = f64(out)
-    assert np.array_equal(got[3], np.zeros_like(got[3]))
-    ref[3] = 0.0
+    for r in (3, 5):
+        assert np.array_equal(got[r], np.zeros_like(got[r]))
+        ref[r] = 0.0
     assert_close(got, ref, f"B{B}")
 
 
