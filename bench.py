@@ -435,6 +435,9 @@ def main():
     ap.add_argument("--separate-store", action="store_true",
                     help="time pkv_store_kv + pkv_paged_attn_decode instead of pkv_decode_step")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--only", default="", metavar="WORKLOAD",
+                    help="only time one named workload (for profiler runs of a single "
+                         "kernel), print its timing as JSON and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (a known "
                          "byte count for scaling HBM traffic counters) and exit")
@@ -457,6 +460,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": n, "launches": 5}))
+        return
+    if args.only:
+        r = time_workload(args.only, args.steps, args.warmup, args.split_tokens)
+        wa = r["workload"]
+        rec = {"workload": args.only, "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 2),
+               "ms_per_step": round(r["ms_per_step"], 5), "replicas": r["replicas"]}
+        if wa.kind == "decode":
+            rec["bytes_per_launch"] = decode_bytes(wa) + (store_bytes(wa) if r["fused"] else 0)
+        else:
+            rec["flops_per_launch"] = prefill_flops(wa)
+        print(json.dumps(rec))
         return
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} CUs={props.multi_processor_count} "
