@@ -322,7 +322,7 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
       // Every P is therefore <= 2^kTau, and tiles whose scores stay near the
       // running maximum cost no max reduction.
       if (kt == 0) {
-  #pragma unroll
+#pragma unroll
         for (int nb = 0; nb < NB; ++nb) m[nb] = tile_max(sacc[nb]) * c;
       }
 
@@ -333,16 +333,16 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
       float ts[NB];
       auto probs = [&](const f32x16 (&src)[NB][2]) {
         bool over = false;
-  #pragma unroll
+#pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const float nm = -m[nb];
           float t[2] = {0.f, 0.f};
-  #pragma unroll
+#pragma unroll
           for (int kh = 0; kh < 2; ++kh)
-  #pragma unroll
+#pragma unroll
             for (int u = 0; u < 2; ++u) {
               uint32_t w[4];
-  #pragma unroll
+#pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const float e0 = fast_exp2(__builtin_fmaf(src[nb][kh][8 * u + 2 * j], c, nm));
                 const float e1 = fast_exp2(__builtin_fmaf(src[nb][kh][8 * u + 2 * j + 1], c, nm));
@@ -361,22 +361,22 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
         // Rare: recompute the tile's scores (the exponentials consumed them),
         // move the reference, rescale, recompute P.
         f32x16 rs[NB][2];
-  #pragma unroll
+#pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-  #pragma unroll
+#pragma unroll
           for (int kh = 0; kh < 2; ++kh)
-  #pragma unroll
+#pragma unroll
             for (int v = 0; v < 16; ++v) rs[nb][kh][v] = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-  #pragma unroll
+#pragma unroll
           for (int kh = 0; kh < 2; ++kh) {
             const bf16x8 a = as_bf16x8(ld16(&Kt[kh * 32 * PITCH + k_off + 16 * ks]));
-  #pragma unroll
+#pragma unroll
             for (int nb = 0; nb < NB; ++nb)
               rs[nb][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[nb][ks], rs[nb][kh], 0, 0, 0);
           }
-  #pragma unroll
+#pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           if (diag) {
             mask(rs[nb][0], nb, 0);
@@ -385,32 +385,32 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
           const float mn = fmaxf(m[nb], tile_max(rs[nb]) * c);
           const float al = fast_exp2(m[nb] - mn);
           l[nb] *= al;
-  #pragma unroll
+#pragma unroll
           for (int db = 0; db < DB; ++db)
-  #pragma unroll
+#pragma unroll
             for (int v = 0; v < 16; ++v) oacc[db][nb][v] *= al;
           m[nb] = mn;
         }
         probs(rs);
       }
-  #pragma unroll
+#pragma unroll
       for (int nb = 0; nb < NB; ++nb) l[nb] += ts[nb];
 
       // Operand slot (half, i) of step (kh, u) holds key
       // kh*32 + 16u + 8(i/4) + 4*half + i%4 on both sides; the V^T operand
       // comes from two transposing LDS reads of 4 rows each.
-  #pragma unroll
+#pragma unroll
       for (int kh = 0; kh < 2; ++kh)
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < 2; ++u) {
           const uint16_t* vrow = Vt + (kh * 32 + 16 * u) * PITCH + v_off;
-  #pragma unroll
+#pragma unroll
           for (int db = 0; db < DB; ++db) {
             const s16x4 lo = lds_read_tr16(vrow + 32 * db);
             const s16x4 hi = lds_read_tr16(vrow + 8 * PITCH + 32 * db);
             const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-  #pragma unroll
+#pragma unroll
             for (int nb = 0; nb < NB; ++nb)
               oacc[db][nb] =
                   __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kh][u][nb], oacc[db][nb], 0, 0, 0);
@@ -420,11 +420,11 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
       // Column maxima of the raw scores (the scale is positive), lazy rescale.
       bool grow = false;
       float mt[NB];
-  #pragma unroll
+#pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         float a = fmaxf(sacc[nb][0][0], sacc[nb][1][0]);
         float b = fmaxf(sacc[nb][0][1], sacc[nb][1][1]);
-  #pragma unroll
+#pragma unroll
         for (int v = 2; v < 16; v += 2) {
           a = fmaxf(a, fmaxf(sacc[nb][0][v], sacc[nb][1][v]));
           b = fmaxf(b, fmaxf(sacc[nb][0][v + 1], sacc[nb][1][v + 1]));
@@ -433,14 +433,14 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
         grow |= mt[nb] > m[nb] + kTau;
       }
       if (__any(grow)) {
-  #pragma unroll
+#pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const float mn = fmaxf(m[nb], mt[nb]);
           const float al = mn == kNegInf ? 1.f : fast_exp2(m[nb] - mn);
           l[nb] *= al;
-  #pragma unroll
+#pragma unroll
           for (int db = 0; db < DB; ++db)
-  #pragma unroll
+#pragma unroll
             for (int v = 0; v < 16; ++v) oacc[db][nb][v] *= al;
           m[nb] = mn;
         }
@@ -450,16 +450,16 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
       // sums add up the same rounded values.  Operand slot (half, i) of step
       // (kh, u) holds key kh*32 + 16u + 8(i/4) + 4*half + i%4 on both sides;
       // the V^T operand comes from two transposing LDS reads of 4 rows each.
-  #pragma unroll
+#pragma unroll
       for (int kh = 0; kh < 2; ++kh)
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < 2; ++u) {
           bf16x8 pb[NB];
-  #pragma unroll
+#pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const float nm = -m[nb];
             uint32_t w[4];
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float e0 = fast_exp2(__builtin_fmaf(sacc[nb][kh][8 * u + 2 * j], c, nm));
               const float e1 = fast_exp2(__builtin_fmaf(sacc[nb][kh][8 * u + 2 * j + 1], c, nm));
@@ -470,13 +470,13 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
             pb[nb] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
           }
           const uint16_t* vrow = Vt + (kh * 32 + 16 * u) * PITCH + v_off;
-  #pragma unroll
+#pragma unroll
           for (int db = 0; db < DB; ++db) {
             const s16x4 lo = lds_read_tr16(vrow + 32 * db);
             const s16x4 hi = lds_read_tr16(vrow + 8 * PITCH + 32 * db);
             const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-  #pragma unroll
+#pragma unroll
             for (int nb = 0; nb < NB; ++nb)
               oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb], oacc[db][nb], 0, 0, 0);
           }
