@@ -374,7 +374,8 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
             const bf16x8 a = as_bf16x8(ld16(&Kt[kh * 32 * PITCH + k_off + 16 * ks]));
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-              rs[nb][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[nb][ks], rs[nb][kh], 0, 0, 0);
+              rs[nb][kh] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[nb][ks], rs[nb][kh], 0, 0, 0);
           }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -478,7 +479,8 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
             const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-              oacc[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb], oacc[db][nb], 0, 0, 0);
+              oacc[db][nb] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb], oacc[db][nb], 0, 0, 0);
           }
         }
     }
