@@ -12,8 +12,8 @@
 // owns NB blocks of 32 columns.
 //
 // The grid is persistent: as many 256-thread blocks as fit on the device at
-// once, each pulling items from a counter in the caller's workspace, latest
-// query tiles (the longest key ranges) first.  The hardware dispatcher starts
+// once, each pulling items from a counter in the caller's workspace, the
+// longest key ranges first.  The hardware dispatcher starts
 // blocks strictly in grid order, so a grid of one block per item leaves CUs
 // idle behind long-running blocks; pulling keeps every resident block busy
 // until the items run out.  The block that draws the last ticket puts the
@@ -64,6 +64,7 @@ struct PrefillParams {
   int32_t num_kv_heads;
   int32_t n_qtiles;
   int32_t n_items;
+  int32_t longest_first;  // 1: tickets map to (request, query tile) pairs longest first
   uint32_t num_pages_u32;  // min(num_pages, 2^31 - 1): page numbers at or above it read page 0
   uint32_t page_bytes;     // bytes per page of one pool (K or V)
   uint32_t row_bytes;      // bytes per token row (all KV heads)
@@ -94,9 +95,21 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
   return max_xor32(fmaxf(a, b));
 }
 
+// Request r's new tokens [s0, s0 + L) and cached prefix length P, clamped
+// so every access stays inside the buffers.
+__device__ __forceinline__ void request_geometry(const PrefillParams& p, int r, int& s0, int& L,
+                                                 int& P) {
+  int a = p.cu_seqlens[r], b = p.cu_seqlens[r + 1];
+  a = min(max(a, 0), p.num_tokens);
+  b = min(max(b, a), p.num_tokens);
+  s0 = a;
+  L = min(min(b - a, p.max_q_len), p.max_seq_len);
+  P = min(max(p.prefix_lens[r], 0), p.max_seq_len - L);
+}
+
 template <int D, int NB, int G, typename KV>
-__device__ __forceinline__ void attend_item(const PrefillParams& p, int item, int rk_all, int tid,
-                                            int lane, int wave, KV& kv);
+__device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int r, int kvh,
+                                            int tid, int lane, int wave, KV& kv);
 
 template <int D, int NB, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
@@ -113,6 +126,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const int wave = tid >> 6;
   const int rk_all = p.num_seqs * p.num_kv_heads;
 
+  // Longest-first order (at most 64 requests, one per lane): query tile qt of
+  // request r reads P_r + QT*(qt+1) keys, so it is put on level
+  // P_r / QT + qt, and tickets walk the levels from the top; a level holds at
+  // most one tile per request, taken in request order, each for every KV head
+  // (consecutive tickets).  Without it, tickets go query tile by query tile
+  // from the last, which leaves the tiles of long prefixes for the end.
+  int lv_b = 0, lv_n = 0;     // this lane's request: first level, tile count
+  int level = -1, below = 0;  // walk state: current level, tickets above it
+  if (p.longest_first) {
+    if (lane < p.num_seqs) {
+      int s0r, Lr, Pr;
+      request_geometry(p, lane, s0r, Lr, Pr);
+      lv_b = Pr / QT;
+      lv_n = (Lr + QT - 1) / QT;
+    }
+    int top = lv_n > 0 ? lv_b + lv_n - 1 : -1;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) top = max(top, __shfl_xor(top, off));
+    level = uniform(top);
+  }
+
   // Tickets are compared unsigned, so even a counter left non-zero by a
   // misuse only ever yields item numbers inside [0, n_items).
   if (tid == 0) item_slot[0] = atomicAdd(p.counter, 1u);
@@ -128,14 +162,42 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
     if (tid == 0) item_slot[par ^ 1] = atomicAdd(p.counter, 1u);
     par ^= 1;
-    attend_item<D, NB, G>(p, (int)item, rk_all, tid, lane, wave, kv);
+    int qt, r, kvh;
+    if (p.longest_first) {
+      const int t = (int)item / p.num_kv_heads;
+      kvh = (int)item % p.num_kv_heads;
+      uint64_t on = 0;
+      while (level >= 0) {
+        on = __ballot(lv_n > 0 && lv_b <= level && level < lv_b + lv_n);
+        const int cnt = __popcll(on);
+        if (t < below + cnt) break;
+        below += cnt;
+        --level;
+      }
+      if (level >= 0) {
+        // the request of the (t - below)-th set bit of `on`
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(on >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)on, 0));
+        const uint64_t pick = __ballot(((on >> lane) & 1) && rank == t - below);
+        r = uniform(__builtin_ctzll(pick));
+        qt = level - __builtin_amdgcn_readlane(lv_b, r);
+      } else {
+        qt = -1;  // past the last tile: nothing to do
+        r = 0;
+      }
+    } else {
+      qt = p.n_qtiles - 1 - (int)item / rk_all;
+      r = (int)item % rk_all / p.num_kv_heads;
+      kvh = (int)item % p.num_kv_heads;
+    }
+    if (qt >= 0) attend_item<D, NB, G>(p, qt, r, kvh, tid, lane, wave, kv);
     __syncthreads();  // LDS tiles free; the next item number is visible
   }
 }
 
 template <int D, int NB, int G, typename KV>
-__device__ __forceinline__ void attend_item(const PrefillParams& p, int item, int rk_all, int tid,
-                                            int lane, int wave, KV& kv) {
+__device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int r, int kvh,
+                                            int tid, int lane, int wave, KV& kv) {
   constexpr int QT = 128 * NB / G;        // positions per item
   constexpr int KS = D / 16;              // 16-dim steps of QK^T
   constexpr int DB = D / 32;              // 32-dim blocks of the output
@@ -147,17 +209,8 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int item, in
   // head_dim 64; at 128 the exact per-tile maxima measured faster.
   constexpr bool kSpeculative = D == 64;
 
-  const int qt = p.n_qtiles - 1 - item / rk_all;  // longest key ranges first
-  const int rk = item % rk_all;
-  const int kvh = rk % p.num_kv_heads;
-  const int r = rk / p.num_kv_heads;
-
-  // Request geometry, clamped so every access stays inside the buffers.
-  int s0 = p.cu_seqlens[r], s1 = p.cu_seqlens[r + 1];
-  s0 = min(max(s0, 0), p.num_tokens);
-  s1 = min(max(s1, s0), p.num_tokens);
-  const int L = min(min(s1 - s0, p.max_q_len), p.max_seq_len);
-  const int P = min(max(p.prefix_lens[r], 0), p.max_seq_len - L);
+  int s0, L, P;
+  request_geometry(p, r, s0, L, P);
   const int q0 = qt * QT;
   if (q0 >= L) return;
   const int qlast = min(q0 + QT, L) - 1;
@@ -602,6 +655,9 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   p.num_kv_heads = num_kv_heads;
   p.n_qtiles = (int32_t)n_qtiles;
   p.n_items = (int32_t)n_items;
+  // Longest-first tickets need one request per lane, and every block walks
+  // the levels once (at most max_seq_len / qtile + n_qtiles of them).
+  p.longest_first = num_seqs <= 64 && (int64_t)max_seq_len / qtile + n_qtiles <= 1024;
   p.num_pages_u32 = (uint32_t)std::min<int64_t>(num_pages, INT32_MAX);
   p.row_bytes = (uint32_t)(num_kv_heads * head_dim * 2);
   p.page_bytes = (uint32_t)page_bytes;

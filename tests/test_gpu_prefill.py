@@ -190,3 +190,21 @@ def test_prefill_late_score_jump(scale):
     out = run_prefill(w)
     torch.cuda.synchronize()
     print(scale, assert_close(f64(out), ref, f"late score jump, scale {scale}"))
+
+
+@pytest.mark.parametrize("B", [64, 70])
+def test_prefill_many_requests(B):
+    # Work items are handed out longest first (key range of each query tile)
+    # for up to 64 requests and query tile by query tile beyond; both orders
+    # must cover every tile exactly once, with empty requests in between.
+    rng = np.random.default_rng(80 + B)
+    prefix = [int(x) for x in rng.integers(0, 300, B)]
+    qlens = [int(x) for x in rng.integers(0, 140, B)]
+    qlens[3] = 0
+    w = inputs.build_prefill(B, 8, 2, 64, 16, prefix, qlens, seed=81 + B, device="cuda")
+    print(f"prefill many requests: B={B} tokens={w.num_tokens}", flush=True)
+    ref = _oracle(w)
+    run_store(w)
+    out = run_prefill(w)
+    torch.cuda.synchronize()
+    print(B, assert_close(f64(out), ref, f"{B} requests"))
