@@ -20,9 +20,9 @@
 // counter back to zero, ready for the next call on the same workspace.
 //
 // Per 64-key tile:
-//   * K and V rows are fetched through the page table into registers one
-//     tile ahead, then written to LDS: K row-major, V transposed (dim-major)
-//     so that PV operands are key-contiguous.
+//   * K and V rows are fetched through the page table into registers three
+//     tiles ahead and written to LDS (row-major) one tile ahead, while the
+//     step's QK^T MFMAs run.
 //   * S^T = K Q^T with MFMA 32x32x16 bf16 (A = K from LDS, B = Q resident in
 //     registers); lane l owns column l % 32, 32 keys of it per 32x32 block.
 //   * Online softmax per column in base 2.  The first tile sets the
@@ -36,6 +36,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "pkv_common.h"
 
@@ -260,7 +261,7 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
   const int klast = kend - 1;
   const int pmask = p.page_size - 1;
   int pg[LOADS];
-  uint4 kr[LOADS], vr[LOADS];
+  uint4 kr[2][LOADS], vr[2][LOADS];  // rows of two tiles in flight
   auto fetch_pages = [&](int kt) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
@@ -268,24 +269,29 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
       pg[it] = pt[kg >> p.page_shift];
     }
   };
-  auto fetch_rows = [&](int kt) {
+  // Register set `set` (a constant at every call) holds the rows of tile kt.
+  auto fetch_rows = [&](int kt, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int kg = min(kt * kKeys + lrow + ROWS * it, klast);
       const uint32_t page = (uint32_t)pg[it] < p.num_pages_u32 ? (uint32_t)pg[it] : 0u;
       const char* kp = kbase + (uint64_t)page * p.page_bytes + __umul24(kg & pmask, p.row_bytes);
-      kr[it] = ld16(kp);
-      vr[it] = ld16(kp + v_minus_k);
+      kr[set][it] = ld16(kp);
+      vr[set][it] = ld16(kp + v_minus_k);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
       const int o = (lrow + ROWS * it) * PITCH + lpc * 8;
-      *reinterpret_cast<uint4*>(&kv[buf][0][o]) = kr[it];
-      *reinterpret_cast<uint4*>(&kv[buf][1][o]) = vr[it];
+      *reinterpret_cast<uint4*>(&kv[buf][0][o]) = kr[set][it];
+      *reinterpret_cast<uint4*>(&kv[buf][1][o]) = vr[set][it];
     }
   };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
 
   f32x16 oacc[DB][NB];
   float m[NB], l[NB];
@@ -306,22 +312,25 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
   const int l16 = lane & 15;
   const int v_off = (4 * half + (l16 >> 2)) * PITCH + 16 * ((lane >> 4) & 1) + 4 * (l16 & 3);
 
+  // Tile t's rows sit in register set t & 1 from their fetch (three tiles
+  // ahead) until they are staged in LDS buffer t & 1 (one tile ahead).
   fetch_pages(0);
-  fetch_rows(0);
-  stash(0);
+  fetch_rows(0, Set0{});
+  stash(0, Set0{});
   if (ntiles > 1) {
     fetch_pages(1);
-    fetch_rows(1);
-    if (ntiles > 2) fetch_pages(2);
+    fetch_rows(1, Set1{});
+    if (ntiles > 2) {
+      fetch_pages(2);
+      fetch_rows(2, Set0{});
+      if (ntiles > 3) fetch_pages(3);
+    }
   }
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  auto tile = [&](int kt, auto par_c) {
+    constexpr int par = decltype(par_c)::value;  // kt & 1
+    constexpr int nxt = 1 - par;                 // register set of tiles kt + 1 and kt + 3
     __syncthreads();  // tile kt is in LDS; every wave is done with tile kt - 1
-    if (kt + 1 < ntiles) stash((kt + 1) & 1);
-    if (kt + 2 < ntiles) {
-      fetch_rows(kt + 2);
-      if (kt + 3 < ntiles) fetch_pages(kt + 3);
-    }
     const uint16_t* Kt = kv[kt & 1][0];
     const uint16_t* Vt = kv[kt & 1][1];
 
@@ -343,6 +352,15 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
           sacc[nb][kh] =
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[nb][ks], sacc[nb][kh], 0, 0, 0);
       }
+    }
+
+    // Stage tile kt + 1 and fetch tile kt + 2 while the QK^T MFMAs run: the
+    // address arithmetic and LDS writes issue from the VALU and LDS pipes
+    // beside the matrix core.
+    if (kt + 1 < ntiles) stash(nxt, std::integral_constant<int, nxt>{});
+    if (kt + 3 < ntiles) {
+      fetch_rows(kt + 3, std::integral_constant<int, nxt>{});
+      if (kt + 4 < ntiles) fetch_pages(kt + 4);
     }
 
     // Causal mask, only on tiles that reach past the block's first column:
@@ -537,6 +555,10 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
           }
         }
     }
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile(kt, Set0{});
+    if (kt + 1 < ntiles) tile(kt + 1, Set1{});
   }
 
   // Normalise and write the valid columns: lane holds dims
