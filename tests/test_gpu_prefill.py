@@ -208,3 +208,16 @@ def test_prefill_many_requests(B):
     out = run_prefill(w)
     torch.cuda.synchronize()
     print(B, assert_close(f64(out), ref, f"{B} requests"))
+
+
+def test_prefill_long_prefix_query_tile_order():
+    # 8 query heads per KV head at head_dim 128 give 16-position query tiles;
+    # with a 17,000-token prefix the levels of the longest-first walk exceed
+    # its bound, so the items go query tile by query tile instead.
+    w = inputs.build_prefill(2, 16, 2, 128, 16, [17000, 5], [40, 33], seed=91, device="cuda")
+    print(f"prefill long prefix: max_seq_len={w.max_seq_len}", flush=True)
+    ref = _oracle(w)
+    run_store(w)
+    out = run_prefill(w)
+    torch.cuda.synchronize()
+    print(assert_close(f64(out), ref, "long prefix"))
