@@ -32,6 +32,7 @@ CASES = [
     (8, 2, 64, 128, [1000, 0, 255], [65, 257, 2]),
     (16, 2, 128, 16, [3, 0, 70], [90, 40, 17]),     # 8 query heads per KV head, 16-row tiles
     (8, 1, 128, 32, [50], [33]),
+    (8, 2, 64, 64, [70, 0, 5], [200, 64, 1]),      # 64-row pages: one page per key tile
 ]
 
 
