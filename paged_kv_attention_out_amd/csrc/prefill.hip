@@ -25,10 +25,12 @@
 //     step's QK^T MFMAs run.
 //   * S^T = K Q^T with MFMA 32x32x16 bf16 (A = K from LDS, B = Q resident in
 //     registers); lane l owns column l % 32, 32 keys of it per 32x32 block.
-//   * Online softmax per column in base 2.  The first tile sets the
-//     reference point; later tiles compute P against it speculatively and
-//     are redone exactly only when a probability may exceed 2^kTau.  Tiles
-//     left of the block's diagonal skip the mask.
+//   * Online softmax per column in base 2.  At head_dim 64 the first tile
+//     sets the reference point and later tiles compute P against it
+//     speculatively, redone exactly only when a probability may exceed
+//     2^kTau; at 128 every tile takes its column maxima and rescales lazily
+//     (when they exceed the reference by more than kTau).  Tiles left of the
+//     block's diagonal skip the mask.
 //   * P (rounded to bf16, round-to-nearest-even) stays in registers: the
 //     accumulator layout of S^T is already the B operand layout of
 //     O^T += V^T P^T, with the key order permuted identically on both sides.
