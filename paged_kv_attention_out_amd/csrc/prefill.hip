@@ -25,12 +25,10 @@
 //     step's QK^T MFMAs run.
 //   * S^T = K Q^T with MFMA 32x32x16 bf16 (A = K from LDS, B = Q resident in
 //     registers); lane l owns column l % 32, 32 keys of it per 32x32 block.
-//   * Online softmax per column in base 2.  At head_dim 64 the first tile
-//     sets the reference point and later tiles compute P against it
-//     speculatively, redone exactly only when a probability may exceed
-//     2^kTau; at 128 every tile takes its column maxima and rescales lazily
-//     (when they exceed the reference by more than kTau).  Tiles left of the
-//     block's diagonal skip the mask.
+//   * Online softmax per column in base 2.  The first tile sets the
+//     reference point; later tiles compute P against it speculatively and
+//     are redone exactly only when a probability may exceed 2^kTau.  Tiles
+//     left of the block's diagonal skip the mask.
 //   * P (rounded to bf16, round-to-nearest-even) stays in registers: the
 //     accumulator layout of S^T is already the B operand layout of
 //     O^T += V^T P^T, with the key order permuted identically on both sides.
@@ -68,7 +66,7 @@ struct PrefillParams {
   int32_t n_qtiles;
   int32_t n_items;
   int32_t longest_first;  // 1: tickets map to (request, query tile) pairs longest first
-  uint32_t num_pages_u32;  // min(num_pages, 2^31 - 1): page numbers at or above it read its last page
+  uint32_t num_pages_u32;  // min(num_pages, 2^31 - 1); larger page numbers read its last page
   uint32_t page_bytes;     // bytes per page of one pool (K or V)
   uint32_t row_bytes;      // bytes per token row (all KV heads)
   float scale_log2;
@@ -76,7 +74,9 @@ struct PrefillParams {
 
 constexpr size_t kPrefillWorkspaceBytes = 256;  // one counter, padded
 constexpr float kTau = 8.0f;
-constexpr float kPmax = 256.0f;  // 2^kTau: a chunk row sum above it may hold a P above 2^kTau
+// 2^kTau: a lane's row sum over a tile above it may hold a P above 2^kTau.
+constexpr float kPmax = 256.0f;
+static_assert(kPmax == (float)(1 << (int)kTau), "kPmax is 2^kTau");
 constexpr int kKeys = 64;  // keys per tile
 
 // fmax over lanes l and l ^ 32 (the two halves of one 32x32 accumulator column).
@@ -208,9 +208,6 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
   constexpr int PIECES = D / 8;           // 16-byte pieces per K/V row
   constexpr int ROWS = 256 / PIECES;      // rows one pass of the block fetches
   constexpr int LOADS = kKeys / ROWS;     // passes per tile
-  // Speculative reference point (no max reduction on most tiles) at
-  // head_dim 64; at 128 the exact per-tile maxima measured faster.
-  constexpr bool kSpeculative = D == 64;
 
   int s0, L, P;
   request_geometry(p, r, s0, L, P);
@@ -268,7 +265,7 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
   // from tile to tile and its page index advances by 64 / page_size, so tiles
   // that lie wholly before the last key need no per-row clamp or offset
   // arithmetic (the last tile of an item takes the general path).
-  const bool small_pages = D == 64 && p.page_size <= kKeys;  // (no gain measured at 128)
+  const bool small_pages = p.page_size <= kKeys;
   const int pstep = kKeys >> p.page_shift;
   const char* kin[LOADS];
   int pidx0[LOADS];
@@ -389,7 +386,7 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
       }
     }
 
-    // Stage tile kt + 1 and fetch tile kt + 2 while the QK^T MFMAs run: the
+    // Stage tile kt + 1 and fetch tile kt + 3 while the QK^T MFMAs run: the
     // address arithmetic and LDS writes issue from the VALU and LDS pipes
     // beside the matrix core.
     if (kt + 1 < ntiles) stash(nxt, std::integral_constant<int, nxt>{});
@@ -417,179 +414,111 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
         for (int kh = 0; kh < 2; ++kh) mask(sacc[nb][kh], nb, kh);
     }
 
-    if constexpr (kSpeculative) {
-      // Reference point of the exponentials.  The first tile sets it to the
-      // column maxima (every column sees key 0, so they are finite).  Later
-      // tiles keep it and compute P speculatively: if a lane's row sum over
-      // the tile shows a probability above 2^kTau (a score more than kTau above
-      // the reference), the tile's scores are recomputed from the K tile still
-      // in LDS, the reference moves to their column maxima, O and l are
-      // rescaled and P is recomputed, all before any P of the tile enters O.
-      // Every P is therefore <= 2^kTau, and tiles whose scores stay near the
-      // running maximum cost no max reduction.
-      if (kt == 0) {
+    // Reference point of the exponentials.  The first tile sets it to the
+    // column maxima (every column sees key 0, so they are finite).  Later
+    // tiles keep it and compute P speculatively: if a lane's row sum over
+    // the tile shows a probability above 2^kTau (a score more than kTau above
+    // the reference), the tile's scores are recomputed from the K tile still
+    // in LDS, the reference moves to their column maxima, O and l are
+    // rescaled and P is recomputed, all before any P of the tile enters O.
+    // Every P is therefore <= 2^kTau, and tiles whose scores stay near the
+    // running maximum cost no max reduction.
+    if (kt == 0) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) m[nb] = tile_max(sacc[nb]) * c;
-      }
+      for (int nb = 0; nb < NB; ++nb) m[nb] = tile_max(sacc[nb]) * c;
+    }
 
-      // P = 2^(s * c - m) in bf16 (the B operands of O^T += V^T P^T, one per
-      // (kh, u) step and column block) and this lane's row sums of the same
-      // rounded values.
-      bf16x8 pb[2][2][NB];
-      float ts[NB];
-      auto probs = [&](const f32x16 (&src)[NB][2]) {
-        bool over = false;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const float nm = -m[nb];
-          float t[2] = {0.f, 0.f};
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              uint32_t w[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float e0 = fast_exp2(__builtin_fmaf(src[nb][kh][8 * u + 2 * j], c, nm));
-                const float e1 = fast_exp2(__builtin_fmaf(src[nb][kh][8 * u + 2 * j + 1], c, nm));
-                w[j] = pack_bf16x2(e0, e1);
-                t[kh] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones,
-                                                        t[kh], false);
-              }
-              pb[kh][u][nb] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-            }
-          ts[nb] = t[0] + t[1];
-          over |= ts[nb] > kPmax;
-        }
-        return over;
-      };
-      if (__any(probs(sacc))) {
-        // Rare: recompute the tile's scores (the exponentials consumed them),
-        // move the reference, rescale, recompute P.
-        f32x16 rs[NB][2];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) rs[nb][kh][v] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            const bf16x8 a = as_bf16x8(ld16(&Kt[kh * 32 * PITCH + k_off + 16 * ks]));
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              rs[nb][kh] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[nb][ks], rs[nb][kh], 0, 0, 0);
-          }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          if (diag) {
-            mask(rs[nb][0], nb, 0);
-            mask(rs[nb][1], nb, 1);
-          }
-          const float mn = fmaxf(m[nb], tile_max(rs[nb]) * c);
-          const float al = fast_exp2(m[nb] - mn);
-          l[nb] *= al;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[db][nb][v] *= al;
-          m[nb] = mn;
-        }
-        probs(rs);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) l[nb] += ts[nb];
-
-      // Operand slot (half, i) of step (kh, u) holds key
-      // kh*32 + 16u + 8(i/4) + 4*half + i%4 on both sides; the V^T operand
-      // comes from two transposing LDS reads of 4 rows each.
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint16_t* vrow = Vt + (kh * 32 + 16 * u) * PITCH + v_off;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const s16x4 lo = lds_read_tr16(vrow + 32 * db);
-            const s16x4 hi = lds_read_tr16(vrow + 8 * PITCH + 32 * db);
-            const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              oacc[db][nb] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kh][u][nb], oacc[db][nb], 0, 0, 0);
-          }
-        }
-    } else {
-      // Column maxima of the raw scores (the scale is positive), lazy rescale.
-      bool grow = false;
-      float mt[NB];
+    // P = 2^(s * c - m) in bf16 (the B operands of O^T += V^T P^T, one per
+    // (kh, u) step and column block) and this lane's row sums of the same
+    // rounded values.
+    bf16x8 pb[2][2][NB];
+    float ts[NB];
+    auto probs = [&](const f32x16 (&src)[NB][2]) {
+      bool over = false;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        float a = fmaxf(sacc[nb][0][0], sacc[nb][1][0]);
-        float b = fmaxf(sacc[nb][0][1], sacc[nb][1][1]);
+        const float nm = -m[nb];
+        float t[2] = {0.f, 0.f};
 #pragma unroll
-        for (int v = 2; v < 16; v += 2) {
-          a = fmaxf(a, fmaxf(sacc[nb][0][v], sacc[nb][1][v]));
-          b = fmaxf(b, fmaxf(sacc[nb][0][v + 1], sacc[nb][1][v + 1]));
-        }
-        mt[nb] = max_xor32(fmaxf(a, b)) * c;
-        grow |= mt[nb] > m[nb] + kTau;
-      }
-      if (__any(grow)) {
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const float mn = fmaxf(m[nb], mt[nb]);
-          const float al = mn == kNegInf ? 1.f : fast_exp2(m[nb] - mn);
-          l[nb] *= al;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[db][nb][v] *= al;
-          m[nb] = mn;
-        }
-      }
-
-      // P = 2^(s * c - m) in bf16 as the B operand of O^T += V^T P^T; the row
-      // sums add up the same rounded values.  Operand slot (half, i) of step
-      // (kh, u) holds key kh*32 + 16u + 8(i/4) + 4*half + i%4 on both sides;
-      // the V^T operand comes from two transposing LDS reads of 4 rows each.
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8 pb[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const float nm = -m[nb];
+          for (int u = 0; u < 2; ++u) {
             uint32_t w[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float e0 = fast_exp2(__builtin_fmaf(sacc[nb][kh][8 * u + 2 * j], c, nm));
-              const float e1 = fast_exp2(__builtin_fmaf(sacc[nb][kh][8 * u + 2 * j + 1], c, nm));
+              const float e0 = fast_exp2(__builtin_fmaf(src[nb][kh][8 * u + 2 * j], c, nm));
+              const float e1 = fast_exp2(__builtin_fmaf(src[nb][kh][8 * u + 2 * j + 1], c, nm));
               w[j] = pack_bf16x2(e0, e1);
-              l[nb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, l[nb],
-                                                      false);
+              t[kh] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones,
+                                                      t[kh], false);
             }
-            pb[nb] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+            pb[kh][u][nb] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
           }
-          const uint16_t* vrow = Vt + (kh * 32 + 16 * u) * PITCH + v_off;
+        ts[nb] = t[0] + t[1];
+        over |= ts[nb] > kPmax;
+      }
+      return over;
+    };
+    if (__any(probs(sacc))) {
+      // Rare: recompute the tile's scores (the exponentials consumed them),
+      // move the reference, rescale, recompute P.
+      f32x16 rs[NB][2];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const s16x4 lo = lds_read_tr16(vrow + 32 * db);
-            const s16x4 hi = lds_read_tr16(vrow + 8 * PITCH + 32 * db);
-            const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              oacc[db][nb] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nb], oacc[db][nb], 0, 0, 0);
-          }
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) rs[nb][kh][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const bf16x8 a = as_bf16x8(ld16(&Kt[kh * 32 * PITCH + k_off + 16 * ks]));
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            rs[nb][kh] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[nb][ks], rs[nb][kh], 0, 0, 0);
         }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (diag) {
+          mask(rs[nb][0], nb, 0);
+          mask(rs[nb][1], nb, 1);
+        }
+        const float mn = fmaxf(m[nb], tile_max(rs[nb]) * c);
+        const float al = fast_exp2(m[nb] - mn);
+        l[nb] *= al;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[db][nb][v] *= al;
+        m[nb] = mn;
+      }
+      probs(rs);
     }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) l[nb] += ts[nb];
+
+    // Operand slot (half, i) of step (kh, u) holds key
+    // kh*32 + 16u + 8(i/4) + 4*half + i%4 on both sides; the V^T operand
+    // comes from two transposing LDS reads of 4 rows each.
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint16_t* vrow = Vt + (kh * 32 + 16 * u) * PITCH + v_off;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const s16x4 lo = lds_read_tr16(vrow + 32 * db);
+          const s16x4 hi = lds_read_tr16(vrow + 8 * PITCH + 32 * db);
+          const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            oacc[db][nb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kh][u][nb], oacc[db][nb], 0, 0, 0);
+        }
+      }
   };
   for (int kt = 0; kt < ntiles; kt += 2) {
     tile(kt, Set0{});

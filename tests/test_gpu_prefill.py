@@ -167,13 +167,14 @@ def test_prefill_extreme_scores(kind):
     print(kind, assert_close(f64(out), ref, kind))
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [0.125, 1.0])
-def test_prefill_late_score_jump(scale):
+def test_prefill_late_score_jump(scale, d):
     # Keys of the first tiles score near 0 and a few later keys score far
     # above them (+23 in base 2 at scale 1/8, +184 at scale 1: 2^184 is not
     # an fp32 number).  The running reference point of the softmax must move
     # on those tiles before any of their probabilities is accumulated.
-    w = inputs.build_prefill(2, 8, 2, 64, 16, [400, 0], [100, 200], seed=71)
+    w = inputs.build_prefill(2, 8, 2, d, 16, [400, 0], [100, 200], seed=71)
     g = torch.Generator().manual_seed(72)
     w.q = torch.ones_like(w.q.float()).to(torch.bfloat16)
     w.k_cache = (w.k_cache.float() * 0.1).to(torch.bfloat16)
@@ -185,7 +186,7 @@ def test_prefill_late_score_jump(scale):
         kc[slot, kvh] = 2.0 + 0.01 * torch.randn(w.head_dim, generator=g)
     w.scale = scale
     w = w.to("cuda")
-    print(f"prefill late score jump: scale {scale}", flush=True)
+    print(f"prefill late score jump: scale {scale}, head_dim {d}", flush=True)
     ref = _oracle(w)
     run_store(w)
     out = run_prefill(w)
