@@ -31,6 +31,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 MIN_WORKING_SET = 1 << 30
+MIN_WARM_S = 0.25  # seconds of back-to-back calls before any timed pass
 METRIC = "paged decode attn HBM GB/s (% peak) + causal prefill attn TFLOP/s (% peak)"
 PRIMARY = "llama_decode"
 
@@ -138,8 +139,26 @@ def _replicate(w, R):
     return reps
 
 
+def warm_up(step, warmup: int, min_s: float = MIN_WARM_S):
+    """Run step(i) for the requested warm-up steps, then more until min_s
+    seconds of back-to-back calls have run, so the timed passes see the GPU
+    at its steady clocks (a short burst times a compute-bound kernel while
+    the clocks are still ramping up).  min_s = 0: exactly `warmup` steps."""
+    import torch
+
+    t_w = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t_w < min_s:
+        step(i)
+        i += 1
+        if i % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
-                  fused_store: bool = True, via_prefill: bool = False):
+                  fused_store: bool = True, via_prefill: bool = False,
+                  min_warm_s: float = MIN_WARM_S):
     """Time one workload's attention call.  A multi-token decode workload runs
     pkv_paged_attn_decode_multi, or with ``via_prefill`` the same batch through
     pkv_paged_attn_prefill (q_len new tokens after a cached prefix of n - q_len)."""
@@ -222,9 +241,7 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
         if ev is not None:
             ev[1].record()
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_up(step, warmup, min_warm_s)
     # Whole-step throughput: K steps between two synchronisations, nothing
     # else enqueued.
     t0 = time.perf_counter()
@@ -277,9 +294,7 @@ def time_store(name: str, steps: int, warmup: int):
                                w.k_cache.shape[0] * w.page_size, w.num_kv_heads, w.head_dim,
                                stream)))
     f = lib.pkv_store_kv
-    for i in range(warmup):
-        f(*calls[i % R][2])
-    torch.cuda.synchronize()
+    warm_up(lambda i: f(*calls[i % R][2]), warmup)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for i in range(steps):
@@ -325,9 +340,7 @@ def time_graph_step(name: str, steps: int, warmup: int):
         with torch.cuda.graph(g):
             step(c, out)
         graphs.append(g)
-    for i in range(warmup):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
+    warm_up(lambda i: graphs[i % R].replay(), warmup)
     t0 = time.perf_counter()
     for i in range(steps):
         graphs[i % R].replay()
@@ -427,7 +440,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -476,8 +489,9 @@ def main():
     log(f"device: {props.name} CUs={props.multi_processor_count} "
         f"arch={getattr(props, 'gcnArchName', '?')} lib={pkv.version()}")
 
+    # the primary line: exactly --warmup untimed steps, then exactly --steps
     r = time_workload(args.workload, args.steps, args.warmup, args.split_tokens,
-                      fused_store=not args.separate_store)
+                      fused_store=not args.separate_store, min_warm_s=0.0)
     w = r["workload"]
     if w.kind != "decode":
         raise SystemExit("the primary line is a decode workload")
