@@ -139,6 +139,39 @@ def _replicate(w, R):
     return reps
 
 
+def segment_trace(path: str, gap_ms: float = 20.0):
+    """Print per-workload statistics of the attention and store kernels in a
+    rocprofv3 kernel-trace CSV of this script: the workloads run one after
+    another, separated by input generation, so dispatches of one kernel
+    more than gap_ms apart start a new segment (segments follow the order
+    in which main() times the workloads)."""
+    import collections
+    import csv
+
+    by = collections.defaultdict(list)
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            by[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    keep = ("prefill_kernel", "decode_split_kernel", "decode_combine_kernel", "store_kv_kernel")
+    for name, v in by.items():
+        short = next((k for k in keep if k in name), None)
+        if short is None:
+            continue
+        tmpl = name[name.find(short) + len(short):].split("(")[0]
+        v.sort()
+        segs, cur = [], [v[0]]
+        for a, b in zip(v, v[1:]):
+            if b[0] - a[1] > gap_ms * 1e6:
+                segs.append(cur)
+                cur = []
+            cur.append(b)
+        segs.append(cur)
+        for i, sg in enumerate(segs):
+            d = sorted((e - s0) / 1e3 for s0, e in sg)
+            print(f"{short + tmpl:34s} segment {i}: calls {len(d):6d}  mean {sum(d) / len(d):9.2f} us"
+                  f"  median {d[len(d) // 2]:9.2f}  min {d[0]:9.2f}  max {d[-1]:9.2f}")
+
+
 def warm_up(step, warmup: int, min_s: float = MIN_WARM_S):
     """Run step(i) for the requested warm-up steps, then more until min_s
     seconds of back-to-back calls have run, so the timed passes see the GPU
@@ -454,7 +487,13 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (a known "
                          "byte count for scaling HBM traffic counters) and exit")
+    ap.add_argument("--segment-trace", default=None, metavar="CSV",
+                    help="only summarise a rocprofv3 kernel-trace CSV of this script per "
+                         "workload (no GPU use) and exit")
     args = ap.parse_args()
+    if args.segment_trace:
+        segment_trace(args.segment_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path runs on a single MI355X)", file=sys.stderr)
