@@ -261,9 +261,10 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
 
   const int lane = threadIdx.x & 63;
   // Block -> unit: rank = block / (Hkv * slices) walks the (request, split) pairs that
-  // exist -- request-major, each request with max(ceil(n / split), 1)
-  // splits -- so every block of the grid past the last pair sits at its end
-  // and the dispatcher starts real units first.  The KV head is the fastest
+  // exist -- each request has max(ceil(n / split), 1) splits; the full-length
+  // ones come first, request-major, then each request's short last split --
+  // so every block of the grid past the last pair sits at its end and the
+  // dispatcher starts real units first.  The KV head is the fastest
   // index: the heads of one (request, split) sweep the same pages together.
   // It rotates from one rank to the next because blocks land on the 8 XCDs
   // round-robin: every XCD then sees every head's offset within the page rows.
@@ -301,30 +302,40 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   if (p.ws_split != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *p.ws_split = sl;
   int r = -1, split = 0, n = 0;
   {
-    int base = 0;  // pairs of the requests before this chunk of 64
-    for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
+    // Units in two parts: first every full-length split of every request
+    // (request-major), then the short last split of each request whose
+    // length is not a multiple of the split (and the one unit of an empty
+    // request), so that the grid ends with its shortest units and the last
+    // round of a multi-round launch drains quickly.
+    auto chunk_len = [&](int c0) -> int {  // -1: no request
       const int k = c0 >> 6;
-      int len;  // -1: no request
-      if (k < 4) {
-        len = k == 0 ? lens.v[0] : k == 1 ? lens.v[1] : k == 2 ? lens.v[2] : lens.v[3];
-      } else {
-        const int rr = c0 + lane;
-        len = rr < p.num_seqs ? min(max(p.seq_lens[rr], 0), p.max_seq_len) : -1;
+      if (k < 4) return k == 0 ? lens.v[0] : k == 1 ? lens.v[1] : k == 2 ? lens.v[2] : lens.v[3];
+      const int rr = c0 + lane;
+      return rr < p.num_seqs ? min(max(p.seq_lens[rr], 0), p.max_seq_len) : -1;
+    };
+    int target = (int)rank;
+    for (int part = 0; part < 2 && r < 0; ++part) {
+      int base = 0;  // units of the requests before this chunk of 64
+      for (int c0 = 0; c0 < p.num_seqs; c0 += 64) {
+        const int len = chunk_len(c0);
+        const int full = len < 0 ? 0 : len / sl;
+        const int cnt = part == 0 ? full : (len == 0 || (len > 0 && len != full * sl)) ? 1 : 0;
+        const int inc = wave_incl_scan(cnt);
+        const int total = __builtin_amdgcn_readlane(inc, 63);
+        if (target < base + total) {
+          const int rel = target - base;
+          const uint64_t hit = __ballot(rel >= inc - cnt && rel < inc);
+          if (hit == 0) break;  // (cannot happen: the unit lies in this chunk)
+          const int lr = (int)__builtin_ctzll(hit);
+          r = c0 + lr;
+          split = part == 0 ? rel - __builtin_amdgcn_readlane(inc - cnt, lr)
+                            : __builtin_amdgcn_readlane(full, lr);
+          n = __builtin_amdgcn_readlane(len, lr);
+          break;
+        }
+        base += total;
       }
-      const int cnt = len < 0 ? 0 : len == 0 ? 1 : (len + sl - 1) / sl;
-      const int inc = wave_incl_scan(cnt);
-      const int total = __builtin_amdgcn_readlane(inc, 63);
-      if ((int)rank < base + total) {
-        const int rel = (int)rank - base;
-        const uint64_t hit = __ballot(rel >= inc - cnt && rel < inc);
-        if (hit == 0) break;  // (cannot happen: rank lies in this chunk)
-        const int lr = (int)__builtin_ctzll(hit);
-        r = c0 + lr;
-        split = rel - __builtin_amdgcn_readlane(inc - cnt, lr);
-        n = __builtin_amdgcn_readlane(len, lr);
-        break;
-      }
-      base += total;
+      target -= base;
     }
   }
   if (r < 0) return;  // past the last pair
