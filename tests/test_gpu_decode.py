@@ -349,3 +349,33 @@ def test_decode_merge_of_many_splits():
     out = run_decode(w)
     torch.cuda.synchronize()
     assert_close(f64(out), ref, "many splits")
+
+
+@pytest.mark.parametrize("split", [64, 128])
+def test_decode_unit_order_many_requests(split):
+    """Blocks take the full-length splits of all requests first and each
+    request's short last split after them.  300 requests (five chunks of 64
+    lengths, the last one read past the first 256) with lengths that are
+    exact multiples of the split, one token past one, empty and negative,
+    at an explicit split: every element against the oracle."""
+    B, hq, hkv, d, ps = 300, 8, 2, 64, 16
+    rng = np.random.default_rng(split + 5)
+    lens = rng.integers(1, 400, size=B).astype(np.int32)
+    lens[::7] = split * rng.integers(1, 5, size=len(lens[::7]))   # whole splits only
+    lens[3::11] = split + 1                                        # one token into a split
+    lens[5] = 0
+    lens[290] = 0
+    w = inputs.build_decode(B, hq, hkv, d, ps, lens, seed=int(split + B), device="cuda")
+    w.seq_lens[9] = -4
+    print(f"unit order: B={B} split={split}", flush=True)
+    kc, vc = host_pools(w)
+    live = [r for r in range(B) if r not in (5, 9, 290)]
+    ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale,
+                     requests=live)
+    out = run_decode(w, split_tokens=split)
+    torch.cuda.synchronize()
+    got = f64(out)
+    for r in (5, 9, 290):
+        assert np.array_equal(got[r], np.zeros_like(got[r]))
+        ref[r] = 0.0
+    assert_close(got, ref, f"unit order split {split}")
