@@ -13,9 +13,11 @@
 * planted mistakes: each plausible slip in the oracle must trip a pin.
 """
 
+import inspect
 import json
 import math
 import os
+import textwrap
 
 import numpy as np
 import pytest
@@ -81,6 +83,10 @@ class Case:
     def oracle_prefill(self):
         return orc.prefill(self.q, self.cu, self.prefix, self.k_cache,
                            self.v_cache, self.table, self.scale)
+
+    def oracle_prefill_dense(self, heads=None):
+        return orc.prefill_dense(self.q, self.cu, self.prefix, self.k_cache,
+                                 self.v_cache, self.table, self.scale, heads=heads)
 
     def sdpa(self):
         """torch SDPA (float64) on the contiguous data, GQA by repetition."""
@@ -316,6 +322,91 @@ def pin_decode_multi_short_context(seed=19):
     assert np.array_equal(empty, np.zeros_like(empty))
 
 
+# ---- prefill_dense: the block-at-a-time form every GPU prefill test uses ----
+
+def pin_prefill_dense_vs_sdpa(g=2, d=16, ps=16, seed=30):
+    # ragged requests, prefixes that are not page multiples, an empty request
+    c = Case(seed, Hq=2 * g, Hkv=2, d=d, ps=ps, prefix=[0, 5, 17, 33, 9],
+             qlens=[7, 1, 20, 0, 4])
+    np.testing.assert_allclose(c.oracle_prefill_dense(), c.sdpa(), rtol=1e-12, atol=1e-12)
+
+
+def pin_prefill_dense_heads_subset(seed=31):
+    # asked-for heads match SDPA; every other head stays NaN
+    c = Case(seed, Hq=8, Hkv=2, d=8, ps=16, prefix=[3, 0], qlens=[12, 30])
+    got = c.oracle_prefill_dense(heads=[1, 6])
+    ref = c.sdpa()
+    np.testing.assert_allclose(got[:, [1, 6]], ref[:, [1, 6]], rtol=1e-12, atol=1e-12)
+    assert np.isnan(got[:, [0, 2, 3, 4, 5, 7]]).all()
+
+
+def pin_prefill_dense_brute_force_scalar(seed=32):
+    c = Case(seed, Hq=4, Hkv=2, d=4, ps=16, prefix=[2, 0, 5], qlens=[3, 2, 0])
+    got = c.oracle_prefill_dense()
+    for r in range(3):
+        q = _bits_to_t64(c.q[c.cu[r]:c.cu[r + 1]]).tolist()
+        K = _bits_to_t64(c.K[r]).tolist()
+        V = _bits_to_t64(c.V[r]).tolist()
+        for i in range(int(c.qlens[r])):
+            for h in range(4):
+                kvh = h // 2
+                vis = int(c.prefix[r]) + i + 1
+                sc = [sum(q[i][h][e] * K[j][kvh][e] for e in range(4)) * c.scale
+                      for j in range(vis)]
+                mx = max(sc)
+                w = [math.exp(s - mx) for s in sc]
+                tot = sum(w)
+                exp = [sum(w[j] * V[j][kvh][e] for j in range(vis)) / tot for e in range(4)]
+                np.testing.assert_allclose(got[c.cu[r] + i, h], exp, rtol=1e-12, atol=1e-14)
+
+
+def pin_prefill_dense_zero_query_is_mean(seed=33):
+    # q = 0: row i of request r is the mean of V rows 0 .. prefix_r + i
+    c = Case(seed, Hq=4, Hkv=2, d=8, ps=16, prefix=[3, 0, 16], qlens=[5, 9, 17])
+    c.q[:] = 0
+    got = c.oracle_prefill_dense()
+    for r in range(3):
+        Vr = _bits_to_t64(c.V[r]).numpy()
+        for i in range(int(c.qlens[r])):
+            vis = int(c.prefix[r]) + i + 1
+            for h in range(4):
+                np.testing.assert_allclose(got[c.cu[r] + i, h], Vr[:vis, h // 2].mean(axis=0),
+                                           rtol=1e-12, atol=1e-14)
+
+
+def pin_prefill_dense_chunked_matches_full(seed=34):
+    c = Case(seed, Hq=4, Hkv=2, d=8, ps=16, prefix=[0], qlens=[40])
+    full = c.oracle_prefill_dense()
+    part = orc.prefill_dense(c.q[25:], np.array([0, 15], np.int32), np.array([25], np.int32),
+                             c.k_cache, c.v_cache, c.table, c.scale)
+    np.testing.assert_allclose(part, full[25:], rtol=1e-13, atol=1e-15)
+
+
+def pin_prefill_dense_single_key_returns_v(seed=35):
+    c = Case(seed, Hq=2, Hkv=1, d=8, ps=16, prefix=[0], qlens=[1])
+    got = c.oracle_prefill_dense()
+    exp = _bits_to_t64(c.V[0][0]).numpy()
+    assert np.array_equal(got[0, 0], exp[0]) and np.array_equal(got[0, 1], exp[0])
+
+
+def pin_prefill_dense_page_permutation_invariance(seed=36):
+    w = inputs.build_prefill(3, 4, 2, 16, 16, [5, 0, 20], [9, 33, 4], seed=seed)
+    a = _wl_np(w)
+    a["kc"], a["vc"] = orc.store_kv(a["kc"], a["vc"], inputs.bf16_bits(w.k_new),
+                                    inputs.bf16_bits(w.v_new), w.out_loc_np)
+    base = orc.prefill_dense(a["q"], a["cu"], a["prefix"], a["kc"], a["vc"], a["table"],
+                             w.scale)
+    perm = np.random.default_rng(seed).permutation(a["kc"].shape[0])
+    kc2 = np.empty_like(a["kc"])
+    vc2 = np.empty_like(a["vc"])
+    kc2[perm] = a["kc"]
+    vc2[perm] = a["vc"]
+    got = orc.prefill_dense(a["q"], a["cu"], a["prefix"], kc2, vc2,
+                            perm[a["table"]].astype(np.int32), w.scale)
+    assert np.isfinite(base).all()
+    assert np.array_equal(base, got)
+
+
 def _wl_np(w):
     return dict(q=inputs.bf16_bits(w.q), kc=inputs.bf16_bits(w.k_cache),
                 vc=inputs.bf16_bits(w.v_cache), table=w.page_table_np,
@@ -329,7 +420,11 @@ PINS = [pin_store_kv_is_index_assignment, pin_vs_sdpa, pin_decode_vs_sdpa,
         pin_page_permutation_invariance, pin_gqa_is_repeated_mha,
         pin_chunked_prefill_matches_full, pin_decode_is_one_row_prefill,
         pin_golden_cu_seqlens, pin_decode_multi_vs_sdpa,
-        pin_decode_multi_one_token_is_decode, pin_decode_multi_short_context]
+        pin_decode_multi_one_token_is_decode, pin_decode_multi_short_context,
+        pin_prefill_dense_vs_sdpa, pin_prefill_dense_heads_subset,
+        pin_prefill_dense_brute_force_scalar, pin_prefill_dense_zero_query_is_mean,
+        pin_prefill_dense_chunked_matches_full, pin_prefill_dense_single_key_returns_v,
+        pin_prefill_dense_page_permutation_invariance]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -337,9 +432,11 @@ def test_pin(pin):
     pin()
 
 
-@pytest.mark.parametrize("g,d,ps", [(1, 64, 16), (2, 128, 256), (4, 64, 16), (4, 8, 32)])
+@pytest.mark.parametrize("g,d,ps", [(1, 64, 16), (2, 128, 256), (4, 64, 16), (4, 8, 32),
+                                    (8, 64, 16), (8, 128, 32)])
 def test_vs_sdpa_shapes(g, d, ps):
     pin_vs_sdpa(g=g, d=d, ps=ps, seed=100 + g + d + ps)
+    pin_prefill_dense_vs_sdpa(g=g, d=d, ps=ps, seed=200 + g + d + ps)
 
 
 def test_bf16_widening_exact():
@@ -421,6 +518,51 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         except Exception:  # a failed assertion or a crash both count
             caught.append(pin.__name__)
     assert caught, f"no pin notices the planted mistake {name}"
+
+
+# Mistakes planted in the text of one oracle function, the way a slip would
+# be typed: ``old`` becomes ``new`` in that function's source, the function
+# is recompiled against the oracle module's names and swapped in, and at
+# least one pin must fail.  These reach functions (prefill_dense, decode,
+# decode_multi) whose arithmetic the helper-level mutants above do not touch.
+SOURCE_MUTANTS = {
+    "dense_mask_off_by_one": ("prefill_dense", "P, scale)", "P + 1, scale)"),
+    "dense_mask_one_early": ("prefill_dense", "P, scale)", "P - 1, scale)"),
+    "dense_prefix_ignored": ("prefill_dense", "P = int(prefix_lens[r])", "P = 0"),
+    "dense_heads_interleaved": ("prefill_dense", "kv_head_of(h, Hq, Hkv)", "h % Hkv"),
+    "dense_scale_dropped": ("prefill_dense", "P, scale)", "P, 1.0)"),
+    "dense_k_v_swapped": ("prefill_dense", "kr[:, kvh], vr[:, kvh]",
+                          "vr[:, kvh], kr[:, kvh]"),
+    "dense_heads_ignored": ("prefill_dense", "(range(Hq) if heads is None else heads)",
+                            "range(Hq)"),
+    "decode_position_one_early": ("decode", "n - 1, scale)", "n - 2, scale)"),
+    "decode_last_key_dropped": ("decode", "attend(qr[h][None, :], kr[:, kvh], vr[:, kvh]",
+                                "attend(qr[h][None, :], kr[:-1, kvh], vr[:-1, kvh]"),
+    "prefill_row_one_late": ("prefill", "P + int(i), scale)", "P + int(i) + 1, scale)"),
+    "multi_mask_off_by_one": ("decode_multi", "first + t0, scale)", "first + t0 + 1, scale)"),
+    "multi_first_position": ("decode_multi", "first = n - L ", "first = n - L + 1 "),
+}
+
+
+def _source_mutant(name, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(orc, name)))
+    assert old in src, f"{name} no longer contains {old!r}: update the planted mistake"
+    namespace = dict(orc.__dict__)
+    exec(compile(src.replace(old, new, 1), f"<planted mistake in {name}>", "exec"), namespace)
+    return namespace[name]
+
+
+@pytest.mark.parametrize("mutant", sorted(SOURCE_MUTANTS))
+def test_planted_source_mistake_is_caught(mutant, monkeypatch):
+    name, old, new = SOURCE_MUTANTS[mutant]
+    monkeypatch.setattr(orc, name, _source_mutant(name, old, new))
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:  # a failed assertion or a crash both count
+            caught.append(pin.__name__)
+    assert caught, f"no pin notices the planted mistake {mutant}"
 
 
 # ---- step metadata (prepare_prefill / prepare_decode) -------------------------
