@@ -135,7 +135,7 @@ int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *                  page_table_stride * page_size >= max_seq_len
  *   head_dim     : 64 or 128
  *   page_size    : 16, 32, 64, 128 or 256
- *   num_q_heads / num_kv_heads : 1, 2 or 4
+ *   num_q_heads / num_kv_heads : 1, 2, 4 or 8
  *   softmax_scale: finite and > 0 (typically 1/sqrt(head_dim))
  *   split_tokens : 0 = automatic (see pkv_decode_split_tokens), else a
  *                  multiple of 16 in [16, 65536]

@@ -104,6 +104,34 @@ def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
     return t
 
 
+def _shape(t: torch.Tensor, expected, name: str) -> None:
+    """Raise ValueError unless ``t`` has ``len(expected)`` dimensions whose
+    sizes equal the non-None entries of ``expected``."""
+    if t.dim() != len(expected) or any(e is not None and int(s) != int(e)
+                                       for s, e in zip(t.shape, expected)):
+        shown = tuple("*" if e is None else int(e) for e in expected)
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shown}")
+
+
+def _pool_shape(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """(num_pages, page_size, Hkv, d) of the K pool; V must have the same."""
+    _shape(k_cache, (None, None, None, None), "k_cache")
+    _shape(v_cache, tuple(k_cache.shape), "v_cache")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+def _table_rows(page_table: torch.Tensor, num_seqs: int) -> None:
+    _shape(page_table, (None, None), "page_table")
+    if page_table.shape[0] < num_seqs:
+        raise ValueError(f"page_table has {page_table.shape[0]} rows for {num_seqs} sequences")
+
+
+def _numel(t: torch.Tensor, n: int, name: str, at_least: bool = False) -> None:
+    if t.dim() != 1 or (t.numel() < n if at_least else t.numel() != n):
+        want = f"at least {n}" if at_least else f"{n}"
+        raise ValueError(f"{name} must be 1-D with {want} entries, has shape {tuple(t.shape)}")
+
+
 def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -111,6 +139,10 @@ def _stream(t: torch.Tensor):
 def pkv_store_kv(k_new: torch.Tensor, v_new: torch.Tensor, out_loc: torch.Tensor,
                  k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
     """Scatter k_new/v_new ``[T, Hkv, d]`` into pool rows ``out_loc``."""
+    _, _, hkv, hd = _pool_shape(k_cache, v_cache)
+    _numel(out_loc, out_loc.numel(), "out_loc")
+    _shape(k_new, (out_loc.numel(), hkv, hd), "k_new")
+    _shape(v_new, (out_loc.numel(), hkv, hd), "v_new")
     for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, torch.bfloat16, n)
     _dev(out_loc, torch.int32, "out_loc")
@@ -142,12 +174,33 @@ def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
+def _check_decode_shapes(q, k_cache, v_cache, page_table, seq_lens, out, workspace,
+                         q_dims: int = 3):
+    """Shapes of a decode call checked against each other before any launch
+    (q ``[B, Hq, d]``, or ``[B, q_len, Hq, d]`` for multi-token decode)."""
+    _shape(q, (None,) * q_dims, "q")
+    B, hq, d = int(q.shape[0]), int(q.shape[-2]), int(q.shape[-1])
+    _, _, hkv, hd = _pool_shape(k_cache, v_cache)
+    if hd != d:
+        raise ValueError(f"k_cache head_dim {hd} differs from q head_dim {d}")
+    if hkv == 0 or hq % hkv != 0:
+        raise ValueError(f"{hq} query heads are not a multiple of {hkv} KV heads")
+    _table_rows(page_table, B)
+    _numel(seq_lens, B, "seq_lens")
+    if out is not None:
+        _shape(out, tuple(q.shape), "out")
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    return B, hkv, d
+
+
 def pkv_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                           softmax_scale: float, out: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None,
                           split_tokens: int = 0) -> torch.Tensor:
     """Decode attention; q ``[B, Hq, d]`` -> out ``[B, Hq, d]`` (bf16)."""
+    _check_decode_shapes(q, k_cache, v_cache, page_table, seq_lens, out, workspace)
     _dev(q, torch.bfloat16, "q")
     _dev(k_cache, torch.bfloat16, "k_cache")
     _dev(v_cache, torch.bfloat16, "v_cache")
@@ -175,6 +228,10 @@ def pkv_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                     workspace: Optional[torch.Tensor] = None,
                     split_tokens: int = 0) -> torch.Tensor:
     """Store the new token's K/V rows and run decode attention in one call."""
+    B, hkv, d = _check_decode_shapes(q, k_cache, v_cache, page_table, seq_lens, out, workspace)
+    _shape(k_new, (B, hkv, d), "k_new")
+    _shape(v_new, (B, hkv, d), "v_new")
+    _numel(out_loc, B, "out_loc")
     for t, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
                     (v_cache, "v_cache")):
         _dev(t, torch.bfloat16, name)
@@ -212,6 +269,7 @@ def pkv_paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
                                 split_tokens: int = 0) -> torch.Tensor:
     """Multi-token decode; q ``[B, q_len, Hq, d]`` -> out ``[B, q_len, Hq, d]``
     (bf16); query token t of request r sits at position seq_lens[r] - q_len + t."""
+    _check_decode_shapes(q, k_cache, v_cache, page_table, seq_lens, out, workspace, q_dims=4)
     _dev(q, torch.bfloat16, "q")
     _dev(k_cache, torch.bfloat16, "k_cache")
     _dev(v_cache, torch.bfloat16, "v_cache")
@@ -240,6 +298,13 @@ def pkv_prefill_metadata(seq_lens: torch.Tensor, prefix_lens: torch.Tensor,
                          cu_seqlens_q: Optional[torch.Tensor] = None,
                          out_loc: Optional[torch.Tensor] = None):
     """cu_seqlens_q ``[B+1]`` and out_loc ``[max_tokens]`` of a prefill batch."""
+    _numel(seq_lens, seq_lens.numel(), "seq_lens")
+    _numel(prefix_lens, seq_lens.numel(), "prefix_lens")
+    _table_rows(page_table, seq_lens.numel())
+    if cu_seqlens_q is not None:
+        _numel(cu_seqlens_q, seq_lens.numel() + 1, "cu_seqlens_q", at_least=True)
+    if out_loc is not None:
+        _numel(out_loc, max_tokens, "out_loc", at_least=True)
     for t, name in ((seq_lens, "seq_lens"), (prefix_lens, "prefix_lens"),
                     (page_table, "page_table")):
         _dev(t, torch.int32, name)
@@ -260,6 +325,10 @@ def pkv_prefill_metadata(seq_lens: torch.Tensor, prefix_lens: torch.Tensor,
 def pkv_decode_metadata(seq_lens: torch.Tensor, page_table: torch.Tensor, page_size: int,
                         out_loc: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out_loc ``[B]``: the slot of each sequence's newest token."""
+    _numel(seq_lens, seq_lens.numel(), "seq_lens")
+    _table_rows(page_table, seq_lens.numel())
+    if out_loc is not None:
+        _numel(out_loc, seq_lens.numel(), "out_loc", at_least=True)
     _dev(seq_lens, torch.int32, "seq_lens")
     _dev(page_table, torch.int32, "page_table")
     B = seq_lens.numel()
@@ -302,6 +371,17 @@ def pkv_paged_attn_prefill(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
 
     ``workspace`` (uint8, zero before its first use) defaults to one buffer
     per (device, stream)."""
+    _shape(q, (None, None, None), "q")
+    _, _, hkv, hd = _pool_shape(k_cache, v_cache)
+    if hd != q.shape[-1]:
+        raise ValueError(f"k_cache head_dim {hd} differs from q head_dim {q.shape[-1]}")
+    if hkv == 0 or q.shape[1] % hkv != 0:
+        raise ValueError(f"{q.shape[1]} query heads are not a multiple of {hkv} KV heads")
+    _numel(prefix_lens, prefix_lens.numel(), "prefix_lens")
+    _numel(cu_seqlens_q, prefix_lens.numel() + 1, "cu_seqlens_q")
+    _table_rows(page_table, prefix_lens.numel())
+    if out is not None:
+        _shape(out, tuple(q.shape), "out")
     _dev(q, torch.bfloat16, "q")
     _dev(k_cache, torch.bfloat16, "k_cache")
     _dev(v_cache, torch.bfloat16, "v_cache")

@@ -249,7 +249,7 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   constexpr int NBUF = DecodeTraits<D, G>::NBUF;
   constexpr int VPITCH = D + 8;  // LDS row pitch (bf16): conflict-free rows
   constexpr int NC = G * LQ;     // distinct query columns: (query token, query head)
-  static_assert(G == 1 || G == 2 || G == 4, "query heads per KV head");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "query heads per KV head");
   static_assert(NC <= 16 && (16 % NC) == 0, "the 16 MFMA columns hold whole copies of the columns");
   // LDS: NBUF * 16 * VPITCH values per wave, sized at launch.
   extern __shared__ __attribute__((aligned(16))) uint16_t vlds_block[];
@@ -549,15 +549,17 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
     }
   };
 
-  // Main loop over windows of up to 64 pages.  Inside a window the groups
-  // go in chunks of NBUF: every K/V load of a chunk is issued first, then
-  // the pairs of groups are computed in order, each waiting only for its
-  // own rows.  No load is pending across a loop back-edge, so the wait
-  // counts the compiler derives are exact.
-  const int win_tokens = 64 << p.page_shift;
-  for (int w0 = t_begin; w0 < t_end; w0 += win_tokens) {
+  // Main loop over windows of up to 64 pages.  A window ends at the end of
+  // its 64th page (or of the split), never inside a 65th: a split need not
+  // start on a page boundary (split lengths are multiples of 16, pages may
+  // be longer), and the next window then starts at the page boundary.
+  // Inside a window the groups go in chunks of NBUF: every K/V load of a
+  // chunk is issued first, then the pairs of groups are computed in order,
+  // each waiting only for its own rows.  No load is pending across a loop
+  // back-edge, so the wait counts the compiler derives are exact.
+  for (int w0 = t_begin, w_end; w0 < t_end; w0 = w_end) {
     if (w0 != t_begin) load_window(w0 >> p.page_shift);
-    const int w_end = min(t_end, w0 + win_tokens);
+    w_end = (int)min((int64_t)t_end, (int64_t)(lp_base + 64) << p.page_shift);
     const int len = w_end - w0;
     const int tail = len & 15;
     const int nfull = len >> 4;
@@ -859,7 +861,9 @@ int launch_decode_lq(const DecodeParams& p, int lq, int64_t waves, hipStream_t s
   switch (lq) {
     case 1: return launch_decode<D, G, 1>(p, waves, s);
     case 2: return launch_decode<D, G, 2>(p, waves, s);
-    case 4: return launch_decode<D, G, 4>(p, waves, s);
+    case 4:
+      if constexpr (G <= 4) return launch_decode<D, G, 4>(p, waves, s);
+      break;
     case 8:
       if constexpr (G <= 2) return launch_decode<D, G, 8>(p, waves, s);
       break;
@@ -937,7 +941,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   if ((int64_t)page_table_stride * page_size < max_seq_len) return PKV_EINVAL;
   const int g = num_q_heads / num_kv_heads;
   if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
-  if (g != 1 && g != 2 && g != 4) return PKV_EUNSUPPORTED;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return PKV_EUNSUPPORTED;
 
   const int32_t split = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
   const int64_t nsm = (max_seq_len + split - 1) / split;
@@ -992,11 +996,13 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   if (head_dim == 64) {
     if (g == 1) return launch_decode_lq<64, 1>(p, lq, waves, s);
     if (g == 2) return launch_decode_lq<64, 2>(p, lq, waves, s);
-    return launch_decode_lq<64, 4>(p, lq, waves, s);
+    if (g == 4) return launch_decode_lq<64, 4>(p, lq, waves, s);
+    return launch_decode_lq<64, 8>(p, lq, waves, s);
   }
   if (g == 1) return launch_decode_lq<128, 1>(p, lq, waves, s);
   if (g == 2) return launch_decode_lq<128, 2>(p, lq, waves, s);
-  return launch_decode_lq<128, 4>(p, lq, waves, s);
+  if (g == 4) return launch_decode_lq<128, 4>(p, lq, waves, s);
+  return launch_decode_lq<128, 8>(p, lq, waves, s);
 }
 
 }  // namespace

@@ -57,27 +57,41 @@ __device__ __forceinline__ int32_t slot_of(const int32_t* row, int pt_stride, in
   return (s < 0 || s > INT32_MAX) ? -1 : (int32_t)s;
 }
 
-// One 256-thread block per request: the block sums the new-token counts of
-// the requests before it (its offset in the flat batch), then writes the
-// slots of its own new tokens.
-__global__ __launch_bounds__(256) void prefill_meta_kernel(PrefillMetaParams p) {
-  __shared__ int part[256];
+// cu_seqlens by one workgroup: the requests go in chunks of 1024, each
+// chunk scanned in LDS (inclusive, Hillis-Steele) and offset by the total of
+// the chunks before it.  Linear in the number of requests.
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void prefill_cu_kernel(PrefillMetaParams p) {
+  __shared__ int buf[2][kScanThreads];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  if (tid == 0) p.cu_seqlens[0] = 0;
+  for (int r0 = 0; r0 < p.num_seqs; r0 += kScanThreads) {
+    const int r = r0 + tid;
+    int cur = 0;
+    buf[0][tid] = r < p.num_seqs ? new_tokens(p, r) : 0;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+      const int v = buf[cur][tid] + (tid >= off ? buf[cur][tid - off] : 0);
+      buf[cur ^ 1][tid] = v;
+      cur ^= 1;
+      __syncthreads();
+    }
+    if (r < p.num_seqs) p.cu_seqlens[r + 1] = carry + buf[cur][tid];
+    carry += buf[cur][kScanThreads - 1];
+    __syncthreads();  // every thread has read the chunk total before the next chunk
+  }
+}
+
+// One 256-thread block per request: its new tokens start at cu_seqlens[r]
+// (written by prefill_cu_kernel, earlier on the same stream); the block
+// writes their slots.
+__global__ __launch_bounds__(256) void prefill_slots_kernel(PrefillMetaParams p) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  int acc = 0;
-  for (int j = tid; j < r; j += 256) acc += new_tokens(p, j);
-  part[tid] = acc;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) part[tid] += part[tid + off];
-    __syncthreads();
-  }
-  const int start = part[0];
+  const int start = p.cu_seqlens[r];
   const int len = new_tokens(p, r);
-  if (tid == 0) {
-    if (r == 0) p.cu_seqlens[0] = 0;
-    p.cu_seqlens[r + 1] = start + len;
-  }
   const int32_t* row = p.page_table + (int64_t)r * p.pt_stride;
   const int first = max(p.prefix_lens[r], 0);
   for (int i = tid; i < len; i += 256) {
@@ -119,8 +133,10 @@ extern "C" int pkv_prefill_metadata(const int32_t* seq_lens, const int32_t* pref
   p.pt_stride = page_table_stride;
   p.page_size = page_size;
   p.max_tokens = max_tokens;
-  return launch(prefill_meta_kernel, dim3((unsigned)num_seqs), dim3(256),
-                static_cast<hipStream_t>(stream), p);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int st = launch(prefill_cu_kernel, dim3(1), dim3(kScanThreads), s, p);
+  if (st != PKV_OK || max_tokens == 0) return st;
+  return launch(prefill_slots_kernel, dim3((unsigned)num_seqs), dim3(256), s, p);
 }
 
 extern "C" int pkv_decode_metadata(const int32_t* seq_lens, int32_t num_seqs,

@@ -58,9 +58,11 @@ def host_pools(w: inputs.Workload, stored: bool = True):
     return kc, vc
 
 
-def compact(w: inputs.Workload, requests):
+def compact(w: inputs.Workload, requests, kv_head=None):
     """Host bit copies of just the given requests' pages (gathered with torch
-    indexing on the device), with a page table renumbered to match."""
+    indexing on the device), with a page table renumbered to match.  With
+    ``kv_head`` only that KV head's slice of each row is kept (a pool of one
+    KV head)."""
     ps = w.page_size
     rows, tables = [], []
     nxt = 0
@@ -71,8 +73,9 @@ def compact(w: inputs.Workload, requests):
         tables.append(np.arange(nxt, nxt + k, dtype=np.int32))
         nxt += k
     idx = torch.from_numpy(np.concatenate(rows).astype(np.int64)).to(w.k_cache.device)
-    kc = inputs.bf16_bits(w.k_cache[idx])
-    vc = inputs.bf16_bits(w.v_cache[idx])
+    heads = slice(None) if kv_head is None else slice(kv_head, kv_head + 1)
+    kc = inputs.bf16_bits(w.k_cache[idx][:, :, heads].contiguous())
+    vc = inputs.bf16_bits(w.v_cache[idx][:, :, heads].contiguous())
     W = max(len(t) for t in tables)
     table = np.zeros((len(requests), W), np.int32)
     for i, t in enumerate(tables):

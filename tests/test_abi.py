@@ -87,7 +87,7 @@ def _decode(**kw):
     (dict(scale=float("nan")), 1), (dict(stride=127), 1), (dict(pages=0), 1),
     (dict(split=8), 1), (dict(split=17), 1), (dict(split=70000), 1), (dict(q=FAKE + 4), 1),
     (dict(ps=24), 2), (dict(ps=8), 2), (dict(ps=512), 2), (dict(d=96), 2), (dict(d=256), 2),
-    (dict(hq=64), 2),                       # 8 query heads per KV head
+    (dict(hq=128), 2),                      # 16 query heads per KV head
     (dict(wsb=100, ws=FAKE), 3),            # needs a workspace, too small
     (dict(B=0), 0),
 ])
@@ -108,7 +108,7 @@ def _step(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(kn=None), 1), (dict(vn=None), 1), (dict(loc=None), 1), (dict(kn=FAKE + 8), 1),
-    (dict(vn=FAKE + 2), 1), (dict(q=None), 1), (dict(d=96), 2), (dict(hq=64), 2),
+    (dict(vn=FAKE + 2), 1), (dict(q=None), 1), (dict(d=96), 2), (dict(hq=128), 2),
     (dict(wsb=100, ws=FAKE), 3), (dict(B=0, kn=None, vn=None, loc=None), 0),
 ])
 def test_decode_step_validation(kw, status):
@@ -129,7 +129,7 @@ def _multi(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(L=0), 1), (dict(L=17), 1), (dict(L=-3), 1), (dict(q=None), 1), (dict(out=None), 1),
     (dict(seq=None), 1), (dict(scale=0.0), 1), (dict(hq=30), 1), (dict(split=24), 1),
-    (dict(q=FAKE + 2), 1), (dict(d=96), 2), (dict(hq=64), 2), (dict(ps=24), 2),
+    (dict(q=FAKE + 2), 1), (dict(d=96), 2), (dict(hq=128), 2), (dict(ps=24), 2),
     (dict(wsb=100, ws=FAKE), 3), (dict(ws=FAKE + 64, wsb=1 << 30), 1),
     (dict(B=0), 0), (dict(B=0, L=16), 0),
 ])

@@ -1,8 +1,9 @@
 """Paged decode attention on the GPU against the float64 oracle.
 
 Small cases compare every output element; the full-size workloads compare
-every element where the oracle is quick (tiny, Llama-shaped) and sampled
-requests otherwise (Qwen-shaped, long context).  Invariants: physical page
+every element of every request (tiny, Llama- and Qwen-shaped), and for the
+long-context batch every request on the query heads of one KV head each
+(all eight KV heads covered).  Invariants: physical page
 permutation (bit-exact), run-to-run determinism (bit-exact), independence
 of the split length (within tolerance), a single visible token returns its
 V row exactly, zero query gives the mean of V, empty requests give zeros,
@@ -31,6 +32,8 @@ CASES = [
     (3, 8, 8, 128, 16, [40, 1, 300], 32),
     (2, 8, 2, 128, 64, [911, 16], 16),
     (3, 2, 1, 64, 128, [129, 4000, 3], 0),
+    (3, 16, 2, 64, 16, [1, 300, 2000], 0),         # 8 query heads per KV head
+    (3, 32, 4, 128, 32, [17, 900, 3000], 128),
 ]
 
 
@@ -74,21 +77,82 @@ def test_decode_llama_workload():
     print("llama_decode max/mean err", assert_close(f64(out), ref, "llama_decode"))
 
 
-@pytest.mark.parametrize("name,nreq", [("qwen_decode", 12), ("long_decode", 2)])
-def test_decode_large_workload_sampled(name, nreq):
-    print(f"decode workload={name}", flush=True)
-    w = inputs.make_workload(name, device="cuda")
+def test_decode_qwen_workload_every_request():
+    """Qwen-shaped batch (128 requests up to 8192 tokens, 256-row pages):
+    every element of every request against the oracle, 16 requests at a
+    time."""
+    w = inputs.make_workload("qwen_decode", device="cuda")
     out = run_decode(w)
     torch.cuda.synchronize()
-    order = np.argsort(w.seq_lens_np)
-    reqs = sorted(set([int(order[-1]), int(order[0])] +
-                      np.random.default_rng(0).choice(w.num_seqs, nreq, replace=False).tolist()))
-    reqs = reqs[:max(nreq, 2)]
+    got = f64(out)
+    errs = []
+    for r0 in range(0, w.num_seqs, 16):
+        reqs = list(range(r0, min(r0 + 16, w.num_seqs)))
+        kc, vc, table = compact(w, reqs)
+        ref = orc.decode(inputs.bf16_bits(w.q)[reqs], kc, vc, table, w.seq_lens_np[reqs],
+                         w.scale)
+        errs.append(assert_close(got[reqs], ref, f"qwen_decode requests {r0}.."))
+    print("qwen_decode max/mean err per 16 requests", errs)
+
+
+def test_decode_long_workload_every_request():
+    """Long-context batch (16 requests of 32K-131K tokens, 1% of K rows x8):
+    every request against the oracle, one request at a time, on the two
+    query heads of one KV head (request r: KV head r % 8, so all eight KV
+    heads are covered twice)."""
+    w = inputs.make_workload("long_decode", device="cuda")
+    out = run_decode(w)
+    torch.cuda.synchronize()
+    got = f64(out)
+    g, d = w.group, w.head_dim
+    for r in range(w.num_seqs):
+        kvh = r % w.num_kv_heads
+        kc, vc, table = compact(w, [r], kv_head=kvh)
+        q = inputs.bf16_bits(w.q)[[r]][:, kvh * g:(kvh + 1) * g]
+        ref = orc.decode(q, kc, vc, table, w.seq_lens_np[[r]], w.scale)
+        print(f"long_decode request {r} (n={int(w.seq_lens_np[r])}, KV head {kvh})",
+              assert_close(got[[r]][:, kvh * g:(kvh + 1) * g], ref, f"long_decode r{r}"),
+              flush=True)
+
+
+@pytest.mark.parametrize("hq,hkv,d,ps,lens,split", [
+    (4, 2, 128, 256, [32800, 16500, 300], 16400),  # split 1 starts 16 rows into page 64
+    (8, 2, 64, 32, [4200, 2064, 2065], 2064),       # split 1 starts 16 rows into page 64
+    (4, 2, 64, 64, [9000, 4113], 4112),
+    (8, 4, 128, 128, [20000], 2064),
+])
+def test_decode_split_starting_inside_a_page(hq, hkv, d, ps, lens, split):
+    """Splits whose first token is not the first row of a page and that span
+    more than 63 pages: every window must end on a page boundary."""
+    print(f"split inside a page: ps={ps} split={split} lens={lens}", flush=True)
+    w = inputs.build_decode(len(lens), hq, hkv, d, ps, lens, seed=split + ps, device="cuda",
+                            store_new=True)
+    ref = _oracle(w)
+    run_store(w)
+    out = run_decode(w, split_tokens=split)
+    torch.cuda.synchronize()
+    print(assert_close(f64(out), ref, f"ps {ps} split {split}"))
+
+
+def test_decode_automatic_split_not_a_page_multiple():
+    """1024 requests x 8 KV heads with max_seq_len 40000 and 256-row pages:
+    the host's automatic split (20000 tokens) is not a multiple of the page
+    size, so the long requests' second splits start inside a page."""
+    B, hq, hkv, d, ps = 1024, 8, 8, 64, 256
+    rng = np.random.default_rng(1024)
+    lens = rng.integers(1, 257, size=B).astype(np.int32)
+    long_reqs = [3, 500, 1023]
+    lens[long_reqs] = [40000, 36500, 39999]
+    split = pkv.pkv_decode_split_tokens(B, hkv, 40000)
+    assert split % ps != 0, split
+    print(f"automatic split {split} at ps {ps}", flush=True)
+    w = inputs.build_decode(B, hq, hkv, d, ps, lens, seed=1025, device="cuda")
+    out = run_decode(w)
+    torch.cuda.synchronize()
+    reqs = long_reqs + [0, 1, 700]
     kc, vc, table = compact(w, reqs)
-    q = inputs.bf16_bits(w.q)[reqs]
-    ref = orc.decode(q, kc, vc, table, w.seq_lens_np[reqs], w.scale)
-    print(f"{name} requests {reqs} max/mean err",
-          assert_close(f64(out)[reqs], ref, name))
+    ref = orc.decode(inputs.bf16_bits(w.q)[reqs], kc, vc, table, w.seq_lens_np[reqs], w.scale)
+    print(assert_close(f64(out)[reqs], ref, "automatic split"))
 
 
 def test_decode_page_permutation_is_bit_exact():

@@ -33,6 +33,8 @@ CASES = [
     (3, 4, 4, 64, 16, [16, 200, 1111], 16, 0),     # g = 1, tile 16
     (3, 4, 4, 128, 128, [7, 130, 513], 7, 128),    # g = 1, tile 8
     (4, 16, 16, 64, 16, [1, 2, 3, 4], 4, 0),       # every request shorter than or equal to q_len
+    (3, 16, 2, 64, 16, [2, 90, 1200], 2, 64),      # g = 8, tile 2
+    (3, 32, 4, 128, 32, [5, 333, 900], 5, 0),      # g = 8, 3 slices of 2, one padded column
 ]
 
 

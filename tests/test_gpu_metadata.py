@@ -18,7 +18,8 @@ def _table(rng, B, width, pool):
 
 
 @pytest.mark.parametrize("B,ps,width,seed", [(1, 16, 4, 1), (7, 16, 40, 2), (33, 48, 9, 3),
-                                              (300, 256, 3, 4)])
+                                              (300, 256, 3, 4),
+                                              (2500, 16, 3, 8)])   # three chunks of the scan
 def test_prefill_metadata_matches_oracle(B, ps, width, seed):
     rng = np.random.default_rng(seed)
     table = _table(rng, B, width, B * width + 50)

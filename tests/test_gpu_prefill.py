@@ -3,7 +3,7 @@
 Small cases cover every (head_dim, group) instantiation, empty requests,
 one-token requests, ragged query tiles and prefixes that are not page
 multiples; the chunked-prefill workload runs at full size (store, then
-attention) and is compared on a subset of heads.  Invariants: page
+attention) and is compared on every element.  Invariants: page
 permutation (bit-exact), determinism, one visible key returns its V row
 exactly, decode == one-row prefill (two different kernels, within
 tolerance)."""
@@ -60,9 +60,11 @@ def test_prefill_small(case):
 
 
 def test_prefill_chunked_workload():
+    """The chunked-prefill batch at full size (16 requests, ~15K new tokens
+    over prefixes of up to 1024): store, then attention; every element of
+    all 32 query heads against the oracle."""
     w = inputs.make_workload("chunked_prefill", device="cuda")
-    heads = [0, 5, 14, 31]
-    ref = _oracle(w, heads=heads)
+    ref = _oracle(w)
     run_store(w)
     out = run_prefill(w)
     torch.cuda.synchronize()
