@@ -195,6 +195,35 @@ int pkv_decode_step(const void* q, const void* k_new, const void* v_new,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_decode_step_noalloc -- pkv_decode_step for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call allocates nothing: the
+ * per-split partial results go to a fixed scratch array of the library
+ * (pkv_decode_step_noalloc_max_bytes() bytes on each GPU, held from the
+ * first call on that GPU until the process ends) instead of a caller
+ * workspace.
+ *
+ * Arguments, result and errors are those of pkv_decode_step without
+ * workspace and workspace_bytes.  A call whose arguments need more than
+ * the scratch holds (pkv_decode_workspace_bytes(...) above the maximum)
+ * returns PKV_ENOSPACE before anything is enqueued; PKV_EHIP if the
+ * scratch array's device address cannot be found.  Every call on one GPU
+ * shares that GPU's scratch, which keeps the last call's partials (nothing
+ * in it needs to start at zero): calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race.
+ */
+int pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                            const int32_t* out_loc, void* k_cache, void* v_cache,
+                            int32_t page_size, int64_t num_pages, const int32_t* page_table,
+                            int32_t page_table_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t max_seq_len, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                            int32_t split_tokens, void* out, void* stream);
+
+/* Bytes of the scratch array pkv_decode_step_noalloc uses on each GPU. */
+size_t pkv_decode_step_noalloc_max_bytes(void);
+
+/*
  * pkv_decode_multi_workspace_bytes -- size of the workspace
  * pkv_paged_attn_decode_multi needs (0 when every request fits one split,
  * and on invalid arguments).  Pass the same split_tokens as to the call.

@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     pkv_decode_metadata,
     pkv_decode_multi_workspace_bytes,
     pkv_decode_step,
+    pkv_decode_step_noalloc,
+    pkv_decode_step_noalloc_max_bytes,
     pkv_decode_workspace_bytes,
     pkv_paged_attn_decode,
     pkv_paged_attn_decode_multi,

@@ -45,6 +45,11 @@ SIGNATURES = {
         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
         _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p,
         _c_void_p, _size, _c_void_p]),
+    "pkv_decode_step_noalloc": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
+        _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p,
+        _c_void_p]),
+    "pkv_decode_step_noalloc_max_bytes": (_size, []),
     "pkv_decode_multi_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_decode_multi": (ctypes.c_int, [
         _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _i32, _c_void_p, _i32,
@@ -251,6 +256,35 @@ def pkv_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
         Hkv, d, softmax_scale, split_tokens, _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
         "pkv_decode_step")
     return out
+
+
+def pkv_decode_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            out_loc: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                            softmax_scale: float, out: torch.Tensor,
+                            split_tokens: int = 0) -> torch.Tensor:
+    """pkv_decode_step with the library's fixed scratch instead of a
+    workspace; the caller passes ``out`` (nothing is allocated)."""
+    B, hkv, d = _check_decode_shapes(q, k_cache, v_cache, page_table, seq_lens, out, None)
+    _shape(k_new, (B, hkv, d), "k_new")
+    _shape(v_new, (B, hkv, d), "v_new")
+    _numel(out_loc, B, "out_loc")
+    for t, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                    (v_cache, "v_cache"), (out, "out")):
+        _dev(t, torch.bfloat16, name)
+    for t, name in ((out_loc, "out_loc"), (page_table, "page_table"), (seq_lens, "seq_lens")):
+        _dev(t, torch.int32, name)
+    Hq = q.shape[1]
+    num_pages, ps = k_cache.shape[0], k_cache.shape[1]
+    _check(lib().pkv_decode_step_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out_loc), _ptr(k_cache), _ptr(v_cache), ps,
+        num_pages, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, max_seq_len, Hq,
+        hkv, d, softmax_scale, split_tokens, _ptr(out), _stream(q)), "pkv_decode_step_noalloc")
+    return out
+
+
+def pkv_decode_step_noalloc_max_bytes() -> int:
+    return int(lib().pkv_decode_step_noalloc_max_bytes())
 
 
 def pkv_decode_multi_workspace_bytes(num_seqs: int, q_len: int, num_q_heads: int,

@@ -913,6 +913,36 @@ extern "C" size_t pkv_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_l
       .total;
 }
 
+// ---- decode step without a caller workspace ----------------------------------
+//
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops): the split partials live in a fixed array
+// of this library instead of a caller workspace.  Each GPU the library runs
+// on holds its own copy until the process ends.  Its address is looked up
+// once per device with that device current and kept; the array's name is a
+// host-side stand-in and is never passed to a kernel.
+
+constexpr size_t kScratchBytes = size_t(32) << 20;  // 32 MiB per device
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of this device's copy of `scratch` (null if it cannot be
+// found).  Looked up on the first call on each device.
+void* scratch_on_current_device() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  ptrs[dev].store(p, std::memory_order_release);  // every thread finds the same address
+  return p;
+}
+
+}  // namespace
+
 namespace {
 
 int decode_impl(const void* q, const void* k_new, const void* v_new, const int32_t* out_loc,
@@ -921,7 +951,8 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
                 int32_t num_seqs, int32_t q_len, int32_t max_seq_len, int32_t num_q_heads,
                 int32_t num_kv_heads,
                 int32_t head_dim, float softmax_scale, int32_t split_tokens, void* out,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream,
+                bool use_scratch = false) {
   using namespace pkv_host;
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                        split_tokens))
@@ -951,6 +982,12 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   DecodeParams p = {};
   if (nsm > 1) {
     const WsLayout w = ws_layout(rk, nsm, (int64_t)g * q_len, head_dim);
+    if (use_scratch) {  // the library's fixed scratch instead of a caller workspace
+      workspace_bytes = kScratchBytes;
+      if (workspace_bytes < w.total) return PKV_ENOSPACE;
+      workspace = scratch_on_current_device();
+      if (workspace == nullptr) return PKV_EHIP;
+    }
     if (workspace_bytes < w.total) return PKV_ENOSPACE;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return PKV_EINVAL;
     char* ws = static_cast<char*>(workspace);
@@ -1049,4 +1086,24 @@ extern "C" int pkv_paged_attn_decode_multi(const void* q, int32_t q_len, const v
                      page_table, page_table_stride, seq_lens, num_seqs, q_len, max_seq_len,
                      num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
                      workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t pkv_decode_step_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                       const int32_t* out_loc, void* k_cache, void* v_cache,
+                                       int32_t page_size, int64_t num_pages,
+                                       const int32_t* page_table, int32_t page_table_stride,
+                                       const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t max_seq_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       float softmax_scale, int32_t split_tokens, void* out,
+                                       void* stream) {
+  // Validated exactly as pkv_decode_step; the scratch's address is looked up
+  // only once every argument has passed and the partials fit.
+  if (num_seqs > 0 && (!k_new || !v_new || !out_loc)) return PKV_EINVAL;
+  return decode_impl(q, k_new, v_new, out_loc, k_cache, v_cache, page_size, num_pages,
+                     page_table, page_table_stride, seq_lens, num_seqs, 1, max_seq_len,
+                     num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
+                     nullptr, 0, stream, /*use_scratch=*/true);
 }

@@ -115,6 +115,37 @@ def test_decode_step_validation(kw, status):
     assert _step(**kw) == status
 
 
+def _noalloc(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, loc=FAKE, kc=FAKE, vc=FAKE, ps=16, pages=100, pt=FAKE,
+             stride=128, seq=FAKE, B=4, maxlen=2048, hq=32, hkv=8, d=64, scale=0.125, split=0,
+             out=FAKE, stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_decode_step_noalloc(
+        a["q"], a["kn"], a["vn"], a["loc"], a["kc"], a["vc"], a["ps"], a["pages"], a["pt"],
+        a["stride"], a["seq"], a["B"], a["maxlen"], a["hq"], a["hkv"], a["d"], a["scale"],
+        a["split"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), 1), (dict(loc=None), 1), (dict(q=None), 1), (dict(hq=30), 1),
+    (dict(d=96), 2), (dict(hq=128), 2),
+    # partials beyond the fixed scratch: rejected before anything is enqueued
+    (dict(B=4096, maxlen=131072, stride=8192, hq=32, hkv=8, d=128, split=16), 3),
+    (dict(B=0, kn=None, vn=None, loc=None), 0),
+])
+def test_decode_step_noalloc_validation(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_decode_step_noalloc_scratch_size():
+    cap = pkv.pkv_decode_step_noalloc_max_bytes()
+    assert cap == 32 << 20
+    # the named decode batches fit the scratch at their automatic split
+    for B, hq, hkv, d, maxlen in ((64, 32, 8, 64, 2048), (128, 16, 8, 128, 8192),
+                                  (16, 16, 8, 128, 131072)):
+        assert 0 < pkv.pkv_decode_workspace_bytes(B, hq, hkv, d, maxlen) <= cap
+
+
 def _multi(**kw):
     a = dict(q=FAKE, L=4, kc=FAKE, vc=FAKE, ps=16, pages=100, pt=FAKE, stride=128, seq=FAKE,
              B=4, maxlen=2048, hq=32, hkv=8, d=64, scale=0.125, split=0, out=FAKE, ws=None,
