@@ -341,49 +341,97 @@ def time_store(name: str, steps: int, warmup: int):
             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def time_graph_step(name: str, steps: int, warmup: int):
-    """The decode step (pkv_decode_step) captured once per pool replica in a
-    HIP graph and replayed."""
+def time_graph_buckets(name: str, steps: int, warmup: int,
+                       buckets=(1, 2, 4, 8, 16, 32, 64)):
+    """The decode step captured once per batch-size bucket with
+    pkv_decode_graphs_create over the workload's buffers (sized for the
+    largest bucket), replayed with the first `b` requests live and the rest
+    padded (length 0).  Per bucket: the same live batch as an eager
+    pkv_decode_step call, and the graph replay, each timed back to back by
+    wall clock (host + device) and with HIP events on the stream around each
+    call (device time).  The buffers are not replicated: every bucket's
+    working set is at most the workload's (~150 MB for the Llama-shaped
+    batch), for eager and graph alike."""
+    import ctypes
+
     import torch
 
     import paged_kv_attention_out_amd as pkv
     from paged_kv_attention_out_amd import inputs
 
+    lib = pkv.lib()
     w = inputs.make_workload(name, device="cuda", poison=False)
-    R = max(1, min(64, math.ceil(MIN_WORKING_SET / max(decode_bytes(w), 1))))
-    reps = _replicate(w, R)
-    ws = pkv.decode_workspace(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                              w.max_seq_len)
-    outs = [torch.empty_like(c.q) for c in reps]
+    B, Hq, Hkv, d, ps = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
+    buckets = [b for b in buckets if b <= B]
+    nb = pkv.pkv_decode_graphs_workspace_bytes(buckets, Hq, Hkv, d, w.max_seq_len)
+    ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(w.q)
+    lens = w.seq_lens.clone()
+    graphs = pkv.pkv_decode_graphs_create(buckets, w.q, w.k_cache, w.v_cache, w.page_table,
+                                          w.seq_lens, w.max_seq_len, w.scale, out,
+                                          k_new=w.k_new, v_new=w.v_new, out_loc=w.out_loc,
+                                          workspace=ws)
+    stream = torch.cuda.current_stream().cuda_stream
+    used = ctypes.c_int32(0)
+    res = {}
+    try:
+        for b in buckets:
+            w.seq_lens.copy_(lens)
+            w.seq_lens[b:] = 0           # padding rows: the dummy request
+            torch.cuda.synchronize()
+            at = (w.q.data_ptr(), w.k_new.data_ptr(), w.v_new.data_ptr(), w.out_loc.data_ptr(),
+                  w.k_cache.data_ptr(), w.v_cache.data_ptr(), ps, w.num_pages,
+                  w.page_table.data_ptr(), w.page_table.shape[1], w.seq_lens.data_ptr(), b,
+                  w.max_seq_len, Hq, Hkv, d, w.scale, 0, out.data_ptr(), ws.data_ptr(),
+                  ws.numel(), stream)
 
-    def step(c, out):
-        pkv.pkv_decode_step(c.q, c.k_new, c.v_new, c.out_loc, c.k_cache, c.v_cache,
-                            c.page_table, c.seq_lens, w.max_seq_len, w.scale, out=out,
-                            workspace=ws)
+            def eager(_i):
+                if lib.pkv_decode_step(*at) != 0:
+                    raise RuntimeError("pkv_decode_step failed")
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(reps[0], outs[0])
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graphs = []
-    for c, out in zip(reps, outs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(c, out)
-        graphs.append(g)
-    warm_up(lambda i: graphs[i % R].replay(), warmup)
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    if not torch.isfinite(outs[0].float()).all():
+            def replay(_i):
+                if lib.pkv_decode_graphs_replay(graphs._handle, b, stream,
+                                                ctypes.byref(used)) != 0:
+                    raise RuntimeError("graph replay failed")
+
+            rec = {"live": b, "bytes": int(decode_bytes_rows(w, b))}
+            for kind, fn in (("eager", eager), ("graph", replay)):
+                warm_up(fn, warmup)
+                t0 = time.perf_counter()
+                for i in range(steps):
+                    fn(i)
+                torch.cuda.synchronize()
+                rec[f"{kind}_us_per_step"] = round((time.perf_counter() - t0) * 1e6 / steps, 2)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(steps)]
+                for i in range(steps):
+                    ev[i][0].record()
+                    fn(i)
+                    ev[i][1].record()
+                torch.cuda.synchronize()
+                rec[f"{kind}_gpu_us"] = round(float(np.mean([a.elapsed_time(e) for a, e in ev]))
+                                              * 1e3, 2)
+            if used.value != b:
+                raise RuntimeError(f"bucket {b}: replay used bucket {used.value}")
+            res[str(b)] = rec
+    finally:
+        graphs.destroy()
+        w.seq_lens.copy_(lens)
+    if not torch.isfinite(out.float()).all():
         raise RuntimeError("graph replay: non-finite output")
-    return {"ms_per_step": round(ms, 5), "replicas": R,
-            "GB/s": round((decode_bytes(w) + store_bytes(w)) / (ms * 1e-3) / 1e9, 1),
-            "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1)}
+    return res
+
+
+def decode_bytes_rows(w, rows: int) -> int:
+    """decode_bytes of the first `rows` requests of a decode workload, plus
+    their store_kv rows."""
+    n = w.seq_lens_np[:rows].astype(np.int64)
+    ps = w.page_size
+    kv = int(n.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = 2 * rows * w.num_q_heads * w.head_dim * 2
+    meta = int(((n + ps - 1) // ps).sum()) * 4 + 4 * rows
+    st = 2 * rows * w.num_kv_heads * w.head_dim * 2 * 2 + 4 * rows if w.k_new is not None else 0
+    return kv + qo + meta + st
 
 
 def time_metadata(steps: int):
@@ -430,41 +478,101 @@ def time_metadata(steps: int):
 
 # ---- CPU baseline (the oracle) ------------------------------------------------
 
+def _host_request(w, r):
+    """Host bf16 bits of request r's pages (gathered on the device) and its
+    page-table row renumbered to them."""
+    import torch
+
+    from paged_kv_attention_out_amd import inputs
+
+    ps = w.page_size
+    n = int(w.seq_lens_np[r])
+    k = max((n + ps - 1) // ps, 1)
+    pages = torch.from_numpy(w.page_table_np[r, :k].astype(np.int64)).to(w.k_cache.device)
+    return (inputs.bf16_bits(w.k_cache[pages]), inputs.bf16_bits(w.v_cache[pages]),
+            np.arange(k, dtype=np.int32)[None])
+
+
 def cpu_baseline(name: str, budget_s: float):
-    """Oracle store + decode over whole passes of the batch, until budget_s."""
+    """The float64 CPU oracle on a bounded sample of a workload: requests are
+    taken in order (whole passes over the batch when it is small) until
+    budget_s of oracle time has run.  Decode: store_kv of the request's new
+    row (if any) and decode, in GB/s under the same counting rule as the GPU
+    line.  Prefill: store_kv of the request's new rows and the causal prefill
+    of all its rows and heads, in TFLOP/s of causal-visible pairs and new
+    tokens/s.  Only the oracle calls are timed (host copies of the inputs
+    are not)."""
     import torch
 
     from oracle import paged_attention as orc
     from paged_kv_attention_out_amd import inputs
 
     w = inputs.make_workload(name, device="cuda", poison=False)
-    kc, vc = inputs.bf16_bits(w.k_cache), inputs.bf16_bits(w.v_cache)
-    q = inputs.bf16_bits(w.q)
-    kn = None if w.k_new is None else inputs.bf16_bits(w.k_new)
-    vn = None if w.v_new is None else inputs.bf16_bits(w.v_new)
-    del w.k_cache, w.v_cache
-    torch.cuda.empty_cache()
-    nbytes = decode_bytes(w) + store_bytes(w)
-    passes, done_bytes = 0, 0
-    c0, t0 = time.process_time(), time.perf_counter()
-    while True:
-        if kn is not None:
-            kc2, vc2 = orc.store_kv(kc, vc, kn, vn, w.out_loc_np)
+    small = w.k_cache.numel() * 2 <= (1 << 30)   # keep host copies for later passes
+    cache = {}
+    q_all = inputs.bf16_bits(w.q)
+    kn_all = None if w.k_new is None else inputs.bf16_bits(w.k_new)
+    vn_all = None if w.v_new is None else inputs.bf16_bits(w.v_new)
+    is_decode = w.kind == "decode"
+    multi = is_decode and w.q.dim() == 4
+    ps, hkv, d = w.page_size, w.num_kv_heads, w.head_dim
+    done_bytes = done_flops = done_tokens = 0
+    reqs = 0
+    wall = cpu = 0.0
+    r = 0
+    while wall < budget_s and (r < w.num_seqs or small):
+        rr = r % w.num_seqs
+        kc, vc, row = cache[rr] if rr in cache else _host_request(w, rr)
+        if small:
+            cache[rr] = (kc, vc, row)
+        n = int(w.seq_lens_np[rr])
+        if is_decode:
+            if kn_all is not None:
+                slot = int(orc.slot_of(row[0], n - 1, ps))
+                args = (kn_all[rr:rr + 1], vn_all[rr:rr + 1], np.array([slot], np.int32))
+            c0, t0 = time.process_time(), time.perf_counter()
+            kc2, vc2 = (orc.store_kv(kc, vc, *args) if kn_all is not None else (kc, vc))
+            if multi:
+                orc.decode_multi(q_all[rr:rr + 1], kc2, vc2, row, w.seq_lens_np[rr:rr + 1],
+                                 w.scale)
+            else:
+                orc.decode(q_all[rr:rr + 1], kc2, vc2, row, w.seq_lens_np[rr:rr + 1], w.scale)
+            wall += time.perf_counter() - t0
+            cpu += time.process_time() - c0
+            L = w.q.shape[1] if multi else 1
+            done_bytes += (n * hkv * d * 2 * 2 + 2 * L * w.num_q_heads * d * 2 +
+                           ((n + ps - 1) // ps) * 4 + 4 +
+                           (2 * hkv * d * 2 * 2 + 4 if kn_all is not None else 0))
         else:
-            kc2, vc2 = kc, vc
-        orc.decode(q, kc2, vc2, w.page_table_np, w.seq_lens_np, w.scale)
-        passes += 1
-        done_bytes += nbytes
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
-    return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s",
-            "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"{passes} full pass(es) of store_kv + decode over the {name} batch "
-                      f"(float64 NumPy, {len(os.sched_getaffinity(0))} host cores available); "
-                      f"{wall:.1f} s"}
+            s0, s1 = int(w.cu_seqlens_q[rr]), int(w.cu_seqlens_q[rr + 1])
+            L, P = s1 - s0, int(w.prefix_lens_np[rr])
+            slots = np.array([orc.slot_of(row[0], P + i, ps) for i in range(L)], np.int32)
+            c0, t0 = time.process_time(), time.perf_counter()
+            kc2, vc2 = orc.store_kv(kc, vc, kn_all[s0:s1], vn_all[s0:s1], slots)
+            orc.prefill_dense(q_all[s0:s1], np.array([0, L], np.int32),
+                              np.array([P], np.int32), kc2, vc2, row, w.scale)
+            wall += time.perf_counter() - t0
+            cpu += time.process_time() - c0
+            done_flops += 4 * d * w.num_q_heads * (L * P + L * (L + 1) // 2)
+            done_tokens += L
+        reqs += 1
+        r += 1
+    cores = len(os.sched_getaffinity(0))
+    what = ("store_kv + causal prefill" if not is_decode else
+            ("store_kv + " if kn_all is not None else "") +
+            (f"{w.q.shape[1]}-token decode" if multi else "decode"))
+    rec = {"kind": "oracle", "cores": max(1, round(cpu / max(wall, 1e-9))),
+           "sample": f"{reqs} request(s) of the {name} batch ({w.num_seqs} per batch), "
+                     f"{what}, "
+                     f"float64 NumPy, {cores} host cores available; {wall:.1f} s of oracle time"}
+    if is_decode:
+        rec.update(value=round(done_bytes / wall / 1e9, 4), unit="GB/s")
+    else:
+        rec.update(value=round(done_flops / wall / 1e12, 6), unit="TFLOP/s",
+                   tokens_per_s=round(done_tokens / wall, 1))
+    del w
+    torch.cuda.empty_cache()
+    return rec
 
 
 # ---- main ------------------------------------------------------------------------
@@ -480,7 +588,9 @@ def main():
     ap.add_argument("--no-also", action="store_true")
     ap.add_argument("--separate-store", action="store_true",
                     help="time pkv_store_kv + pkv_paged_attn_decode instead of pkv_decode_step")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for the primary workload (half that for "
+                         "each other workload)")
     ap.add_argument("--only", default="", metavar="WORKLOAD",
                     help="only time one named workload (for profiler runs of a single "
                          "kernel), print its timing as JSON and exit")
@@ -601,8 +711,9 @@ def main():
             del a, wa
         also["store_kv"] = {n: time_store(n, max(20, args.steps // 5), 3)
                             for n in ("llama_decode", "chunked_prefill")}
-        also["llama_decode_graph_step"] = time_graph_step(args.workload, args.steps,
-                                                          args.warmup)
+        also["decode_graph_buckets"] = time_graph_buckets(args.workload,
+                                                          max(20, args.steps // 5),
+                                                          max(3, args.warmup // 20))
         also["metadata"] = time_metadata(max(20, args.steps // 5))
         # multi-token decode (4 draft tokens per request), and the same batch
         # through the prefill kernel for comparison
@@ -628,6 +739,10 @@ def main():
         del r, w
         torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+        if "also" in line:
+            for name in ("qwen_decode", "long_decode", "chunked_prefill",
+                         "shared_prefix_decode", "spec_decode"):
+                line["also"][name]["cpu_baseline"] = cpu_baseline(name, args.cpu_budget / 2)
     print(json.dumps(line), flush=True)
 
 

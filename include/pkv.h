@@ -224,6 +224,70 @@ int pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
 size_t pkv_decode_step_noalloc_max_bytes(void);
 
 /*
+ * Decode-step graphs, one per batch-size bucket.
+ *
+ * The engines capture the decode step in graphs for a set of batch sizes
+ * (e.g. 1, 2, 4, 8, 16, 32, ...), largest first, and at every step replay
+ * the smallest graph that holds the batch: the batch is copied into the
+ * first rows of fixed buffers and the rows past it are padded with a dummy
+ * request (miniVLLM "Engine Architecture", CUDA graph capture and run_model;
+ * mini-sglang "Engine Class", CUDA graph batch sizes and the dummy request
+ * kept at an extra page-table row).
+ *
+ * pkv_decode_graphs_create captures, for each bucket b, one call of
+ * pkv_decode_step (or of pkv_paged_attn_decode when k_new, v_new and
+ * out_loc are all NULL) with num_seqs = b on the given fixed buffers, which
+ * must be sized for the largest bucket (q [B_max, Hq, d], k_new / v_new
+ * [B_max, Hkv, d], out_loc and seq_lens [B_max], page_table
+ * [B_max, page_table_stride], out [B_max, Hq, d]).  The buffers stay owned
+ * by the caller and must outlive the graphs; their contents are read when a
+ * graph is replayed, not at capture.  Every bucket uses one workspace: the
+ * caller's (at least pkv_decode_graphs_workspace_bytes(...) bytes, 256-byte
+ * aligned) or, when workspace is NULL, the fixed scratch of
+ * pkv_decode_step_noalloc.  The automatic split is used (split_tokens = 0).
+ * The graphs belong to the device current at creation.
+ *
+ *   buckets      : num_buckets (1 .. 64) distinct positive batch sizes, any
+ *                  order
+ *   graphs       : receives the handle (NULL on error)
+ *   all others   : as pkv_decode_step, for the largest bucket
+ *
+ * Returns PKV_EINVAL / PKV_EUNSUPPORTED as pkv_decode_step would for the
+ * largest bucket, PKV_ENOSPACE if the workspace (or the fixed scratch) is
+ * too small, PKV_EHIP if capture or instantiation fails; nothing is left
+ * allocated on error.
+ *
+ * pkv_decode_graphs_replay enqueues on `stream` the graph of the smallest
+ * bucket >= num_seqs (the bucket is written to *bucket_used when non-NULL).
+ * Before it, rows num_seqs .. bucket-1 of seq_lens must hold padding
+ * (seq_lens <= 0: the dummy request, which reads and writes nothing and
+ * gets a zero output row).  num_seqs == 0 enqueues nothing; num_seqs above
+ * the largest bucket, or a call on another device -> PKV_EINVAL.  Replays
+ * sharing a workspace (or the fixed scratch) must be ordered.
+ */
+typedef struct pkv_decode_graphs pkv_decode_graphs;
+
+size_t pkv_decode_graphs_workspace_bytes(const int32_t* buckets, int32_t num_buckets,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_seq_len);
+
+int pkv_decode_graphs_create(const int32_t* buckets, int32_t num_buckets, const void* q,
+                             const void* k_new, const void* v_new, const int32_t* out_loc,
+                             void* k_cache, void* v_cache, int32_t page_size,
+                             int64_t num_pages, const int32_t* page_table,
+                             int32_t page_table_stride, const int32_t* seq_lens,
+                             int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, float softmax_scale, void* out,
+                             void* workspace, size_t workspace_bytes,
+                             pkv_decode_graphs** graphs);
+
+int pkv_decode_graphs_replay(pkv_decode_graphs* graphs, int32_t num_seqs, void* stream,
+                             int32_t* bucket_used);
+
+/* Releases the graphs (NULL is a no-op); the caller's buffers are untouched. */
+void pkv_decode_graphs_destroy(pkv_decode_graphs* graphs);
+
+/*
  * pkv_decode_multi_workspace_bytes -- size of the workspace
  * pkv_paged_attn_decode_multi needs (0 when every request fits one split,
  * and on invalid arguments).  Pass the same split_tokens as to the call.

@@ -6,10 +6,13 @@ and the seeded input generators used by the tests and the benchmark.
 """
 
 from ._lib import (  # noqa: F401
+    DecodeGraphs,
     PKVError,
     decode_workspace,
     lib,
     pkv_decode_split_tokens,
+    pkv_decode_graphs_create,
+    pkv_decode_graphs_workspace_bytes,
     pkv_decode_metadata,
     pkv_decode_multi_workspace_bytes,
     pkv_decode_step,

@@ -50,6 +50,14 @@ SIGNATURES = {
         _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p,
         _c_void_p]),
     "pkv_decode_step_noalloc_max_bytes": (_size, []),
+    "pkv_decode_graphs_workspace_bytes": (_size, [_c_void_p, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_graphs_create": (ctypes.c_int, [
+        _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+        _i32, _i64, _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _f32, _c_void_p,
+        _c_void_p, _size, ctypes.POINTER(ctypes.c_void_p)]),
+    "pkv_decode_graphs_replay": (ctypes.c_int, [_c_void_p, _i32, _c_void_p,
+                                                 ctypes.POINTER(ctypes.c_int32)]),
+    "pkv_decode_graphs_destroy": (None, [_c_void_p]),
     "pkv_decode_multi_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_decode_multi": (ctypes.c_int, [
         _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _i32, _c_void_p, _i32,
@@ -285,6 +293,89 @@ def pkv_decode_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
 
 def pkv_decode_step_noalloc_max_bytes() -> int:
     return int(lib().pkv_decode_step_noalloc_max_bytes())
+
+
+def _buckets(buckets):
+    arr = (ctypes.c_int32 * len(buckets))(*[int(b) for b in buckets])
+    return arr, len(buckets)
+
+
+def pkv_decode_graphs_workspace_bytes(buckets, num_q_heads: int, num_kv_heads: int,
+                                      head_dim: int, max_seq_len: int) -> int:
+    arr, n = _buckets(buckets)
+    return int(lib().pkv_decode_graphs_workspace_bytes(arr, n, num_q_heads, num_kv_heads,
+                                                       head_dim, max_seq_len))
+
+
+class DecodeGraphs:
+    """Handle of pkv_decode_graphs_create: one captured decode step per
+    batch-size bucket over fixed buffers sized for the largest bucket.  The
+    buffers (and the workspace) are kept referenced for the graphs' life."""
+
+    def __init__(self, handle, buckets, keep):
+        self._handle = handle
+        self.buckets = sorted(int(b) for b in buckets)
+        self._keep = keep
+
+    def replay(self, num_seqs: int, stream=None) -> int:
+        """Replay the smallest bucket >= num_seqs on the current stream (or
+        ``stream``); returns the bucket used.  Rows num_seqs .. bucket-1 of
+        seq_lens must hold padding (<= 0)."""
+        used = ctypes.c_int32(0)
+        s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        _check(lib().pkv_decode_graphs_replay(self._handle, num_seqs, s, ctypes.byref(used)),
+               "pkv_decode_graphs_replay")
+        return int(used.value)
+
+    def destroy(self) -> None:
+        if self._handle is not None:
+            lib().pkv_decode_graphs_destroy(self._handle)
+            self._handle = None
+            self._keep = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def pkv_decode_graphs_create(buckets, q: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, page_table: torch.Tensor,
+                             seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
+                             out: torch.Tensor, k_new: Optional[torch.Tensor] = None,
+                             v_new: Optional[torch.Tensor] = None,
+                             out_loc: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> DecodeGraphs:
+    """Capture the decode step (fused store when k_new/v_new/out_loc are
+    given) once per bucket over fixed buffers sized for the largest bucket;
+    ``workspace`` None uses the library's fixed scratch."""
+    B, hkv, d = _check_decode_shapes(q, k_cache, v_cache, page_table, seq_lens, out, workspace)
+    if B < max(int(b) for b in buckets):
+        raise ValueError(f"buffers hold {B} rows, fewer than the largest bucket")
+    fused = k_new is not None
+    if fused:
+        _shape(k_new, (B, hkv, d), "k_new")
+        _shape(v_new, (B, hkv, d), "v_new")
+        _numel(out_loc, B, "out_loc")
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            _dev(t, torch.bfloat16, name)
+        _dev(out_loc, torch.int32, "out_loc")
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        _dev(t, torch.bfloat16, name)
+    for t, name in ((page_table, "page_table"), (seq_lens, "seq_lens")):
+        _dev(t, torch.int32, name)
+    arr, n = _buckets(buckets)
+    handle = ctypes.c_void_p()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    num_pages, ps = k_cache.shape[0], k_cache.shape[1]
+    _check(lib().pkv_decode_graphs_create(
+        arr, n, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out_loc), _ptr(k_cache), _ptr(v_cache),
+        ps, num_pages, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), max_seq_len,
+        q.shape[1], hkv, d, softmax_scale, _ptr(out), _ptr(workspace), ws_bytes,
+        ctypes.byref(handle)), "pkv_decode_graphs_create")
+    keep = (q, k_new, v_new, out_loc, k_cache, v_cache, page_table, seq_lens, out, workspace)
+    return DecodeGraphs(handle, buckets, keep)
 
 
 def pkv_decode_multi_workspace_bytes(num_seqs: int, q_len: int, num_q_heads: int,

@@ -33,6 +33,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <new>
 
 #include "pkv_common.h"
 
@@ -1107,3 +1108,169 @@ extern "C" int pkv_decode_step_noalloc(const void* q, const void* k_new, const v
                      num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
                      nullptr, 0, stream, /*use_scratch=*/true);
 }
+
+// ---- decode-step graphs, one per batch-size bucket ---------------------------
+//
+// The engines capture the decode step once per batch-size bucket and, at
+// every step, replay the smallest captured graph that holds the batch, with
+// the batch copied into the first rows of fixed buffers and the rows past it
+// padded by a dummy request (miniVLLM "Engine Architecture", CUDA graph
+// capture and run_model; mini-sglang "Engine Class", CUDA graph batch sizes
+// and the dummy request).  Here a graph holds one pkv_decode_step (or one
+// pkv_paged_attn_decode) over the first `bucket` rows of the caller's fixed
+// buffers; every bucket shares one workspace, sized for the bucket that
+// needs most, or the library's fixed scratch.
+
+struct pkv_decode_graphs {
+  int device;
+  int count;
+  int32_t bucket[64];         // ascending
+  hipGraphExec_t exec[64];
+};
+
+namespace {
+
+constexpr int kMaxGraphBuckets = 64;
+
+// Occupancy queries are made (and cached) before capture, so nothing but
+// kernel launches happens while the capture stream records.
+template <int D, int G>
+void prime_decode_occupancy() {
+  for (int hpb : {1, 2, 4, 8}) (void)resident_waves<D, G, 1>(hpb);
+}
+
+void prime_occupancy(int head_dim, int g) {
+  if (head_dim == 64) {
+    if (g == 1) prime_decode_occupancy<64, 1>();
+    else if (g == 2) prime_decode_occupancy<64, 2>();
+    else if (g == 4) prime_decode_occupancy<64, 4>();
+    else if (g == 8) prime_decode_occupancy<64, 8>();
+  } else if (head_dim == 128) {
+    if (g == 1) prime_decode_occupancy<128, 1>();
+    else if (g == 2) prime_decode_occupancy<128, 2>();
+    else if (g == 4) prime_decode_occupancy<128, 4>();
+    else if (g == 8) prime_decode_occupancy<128, 8>();
+  }
+}
+
+void destroy_graphs(pkv_decode_graphs* g) {
+  if (g == nullptr) return;
+  for (int i = 0; i < g->count; ++i)
+    if (g->exec[i] != nullptr) (void)hipGraphExecDestroy(g->exec[i]);
+  delete g;
+}
+
+}  // namespace
+
+extern "C" size_t pkv_decode_graphs_workspace_bytes(const int32_t* buckets, int32_t num_buckets,
+                                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t head_dim, int32_t max_seq_len) {
+  if (buckets == nullptr || num_buckets <= 0 || num_buckets > kMaxGraphBuckets) return 0;
+  size_t need = 0;
+  for (int i = 0; i < num_buckets; ++i)
+    need = std::max(need, pkv_decode_workspace_bytes(buckets[i], num_q_heads, num_kv_heads,
+                                                     head_dim, max_seq_len, 0));
+  return need;
+}
+
+extern "C" int pkv_decode_graphs_create(
+    const int32_t* buckets, int32_t num_buckets, const void* q, const void* k_new,
+    const void* v_new, const int32_t* out_loc, void* k_cache, void* v_cache, int32_t page_size,
+    int64_t num_pages, const int32_t* page_table, int32_t page_table_stride,
+    const int32_t* seq_lens, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+    pkv_decode_graphs** graphs) {
+  if (graphs == nullptr) return PKV_EINVAL;
+  *graphs = nullptr;
+  if (buckets == nullptr || num_buckets <= 0 || num_buckets > kMaxGraphBuckets) return PKV_EINVAL;
+  int32_t sorted[kMaxGraphBuckets];
+  std::copy(buckets, buckets + num_buckets, sorted);
+  std::sort(sorted, sorted + num_buckets);
+  for (int i = 0; i < num_buckets; ++i)
+    if (sorted[i] <= 0 || (i > 0 && sorted[i] == sorted[i - 1])) return PKV_EINVAL;
+  const bool fused = k_new != nullptr || v_new != nullptr || out_loc != nullptr;
+  if (fused && (!k_new || !v_new || !out_loc)) return PKV_EINVAL;
+  if (!decode_shape_ok(sorted[num_buckets - 1], num_q_heads, num_kv_heads, head_dim,
+                       max_seq_len, 0))
+    return PKV_EINVAL;
+  // One workspace for every bucket: the caller's, or the fixed scratch.
+  const size_t need = pkv_decode_graphs_workspace_bytes(sorted, num_buckets, num_q_heads,
+                                                        num_kv_heads, head_dim, max_seq_len);
+  const bool use_scratch = workspace == nullptr && need > 0;
+  if (use_scratch) {
+    if (need > kScratchBytes) return PKV_ENOSPACE;
+    if (scratch_on_current_device() == nullptr) return PKV_EHIP;
+  } else if (need > 0 && workspace_bytes < need) {
+    return PKV_ENOSPACE;
+  }
+  // Every argument check of the call, on the largest bucket, before capture.
+  const int g = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_EHIP;
+  prime_occupancy(head_dim, g);
+
+  pkv_decode_graphs* set = new (std::nothrow) pkv_decode_graphs{};
+  if (set == nullptr) return PKV_EHIP;
+  set->device = dev;
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) {
+    delete set;
+    return PKV_EHIP;
+  }
+  int status = PKV_OK;
+  // Largest first, as the engines capture them.
+  for (int i = num_buckets - 1; i >= 0 && status == PKV_OK; --i) {
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+      status = PKV_EHIP;
+      break;
+    }
+    const int st = decode_impl(q, k_new, v_new, out_loc, k_cache, v_cache, page_size, num_pages,
+                               page_table, page_table_stride, seq_lens, sorted[i], 1,
+                               max_seq_len, num_q_heads, num_kv_heads, head_dim, softmax_scale,
+                               0, out, workspace, use_scratch ? 0 : workspace_bytes, cs,
+                               use_scratch);
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(cs, &graph);
+    if (st != PKV_OK || e != hipSuccess || graph == nullptr) {
+      status = st != PKV_OK ? st : PKV_EHIP;
+      if (graph != nullptr) (void)hipGraphDestroy(graph);
+      break;
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess || exec == nullptr) {
+      status = PKV_EHIP;
+      break;
+    }
+    set->bucket[i] = sorted[i];
+    set->exec[i] = exec;
+  }
+  (void)hipStreamDestroy(cs);
+  set->count = num_buckets;
+  if (status != PKV_OK) {
+    destroy_graphs(set);
+    return status;
+  }
+  *graphs = set;
+  return PKV_OK;
+}
+
+extern "C" int pkv_decode_graphs_replay(pkv_decode_graphs* graphs, int32_t num_seqs,
+                                        void* stream, int32_t* bucket_used) {
+  if (bucket_used != nullptr) *bucket_used = 0;
+  if (graphs == nullptr || num_seqs < 0) return PKV_EINVAL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_EHIP;
+  if (dev != graphs->device) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  int i = 0;
+  while (i < graphs->count && graphs->bucket[i] < num_seqs) ++i;
+  if (i == graphs->count) return PKV_EINVAL;  // larger than the largest bucket
+  if (hipGraphLaunch(graphs->exec[i], static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PKV_EHIP;
+  if (bucket_used != nullptr) *bucket_used = graphs->bucket[i];
+  return PKV_OK;
+}
+
+extern "C" void pkv_decode_graphs_destroy(pkv_decode_graphs* graphs) { destroy_graphs(graphs); }

@@ -84,6 +84,41 @@ __global__ __launch_bounds__(kScanThreads) void prefill_cu_kernel(PrefillMetaPar
   }
 }
 
+// Batches of up to kScanThreads requests in one launch: the workgroup scans
+// the counts as above, keeps the offsets in LDS, then each wave writes the
+// slots of every 16th request.
+__global__ __launch_bounds__(kScanThreads) void prefill_meta_small_kernel(PrefillMetaParams p) {
+  __shared__ int buf[2][kScanThreads];
+  const int tid = threadIdx.x;
+  const int r = tid;
+  const int cnt = r < p.num_seqs ? new_tokens(p, r) : 0;
+  int cur = 0;
+  buf[0][tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int v = buf[cur][tid] + (tid >= off ? buf[cur][tid - off] : 0);
+    buf[cur ^ 1][tid] = v;
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (tid == 0) p.cu_seqlens[0] = 0;
+  if (r < p.num_seqs) p.cu_seqlens[r + 1] = buf[cur][tid];
+  if (p.max_tokens == 0) return;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int q = wave; q < p.num_seqs; q += kScanThreads / 64) {
+    const int end = buf[cur][q];
+    const int len = q < p.num_seqs ? new_tokens(p, q) : 0;
+    const int start = end - len;
+    const int32_t* row = p.page_table + (int64_t)q * p.pt_stride;
+    const int first = max(p.prefix_lens[q], 0);
+    for (int i = lane; i < len; i += 64) {
+      const int t = start + i;
+      if (t >= p.max_tokens) break;
+      p.out_loc[t] = slot_of(row, p.pt_stride, p.page_size, first + i);
+    }
+  }
+}
+
 // One 256-thread block per request: its new tokens start at cu_seqlens[r]
 // (written by prefill_cu_kernel, earlier on the same stream); the block
 // writes their slots.
@@ -134,6 +169,8 @@ extern "C" int pkv_prefill_metadata(const int32_t* seq_lens, const int32_t* pref
   p.page_size = page_size;
   p.max_tokens = max_tokens;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (num_seqs <= kScanThreads)
+    return launch(prefill_meta_small_kernel, dim3(1), dim3(kScanThreads), s, p);
   const int st = launch(prefill_cu_kernel, dim3(1), dim3(kScanThreads), s, p);
   if (st != PKV_OK || max_tokens == 0) return st;
   return launch(prefill_slots_kernel, dim3((unsigned)num_seqs), dim3(256), s, p);

@@ -146,6 +146,33 @@ def test_decode_step_noalloc_scratch_size():
         assert 0 < pkv.pkv_decode_workspace_bytes(B, hq, hkv, d, maxlen) <= cap
 
 
+def test_decode_graphs_validation():
+    lib = pkv.lib()
+    arr = (ctypes.c_int32 * 3)(1, 2, 4)
+    h = ctypes.c_void_p(123)
+
+    def create(buckets=arr, n=3, ws=FAKE, wsb=1 << 30, out_ptr=ctypes.byref(h), hq=32, kn=FAKE):
+        return lib.pkv_decode_graphs_create(buckets, n, FAKE, kn, FAKE, FAKE, FAKE, FAKE, 16,
+                                            100, FAKE, 128, FAKE, 2048, hq, 8, 64, 0.125, FAKE,
+                                            ws, wsb, out_ptr)
+
+    assert create(out_ptr=None) == 1
+    assert create(buckets=None) == 1 and h.value is None     # handle cleared on error
+    assert create(n=0) == 1
+    assert create(n=65) == 1
+    assert create(buckets=(ctypes.c_int32 * 3)(1, 2, 2)) == 1  # duplicate bucket
+    assert create(buckets=(ctypes.c_int32 * 2)(0, 4), n=2) == 1
+    assert create(hq=30) == 1
+    assert create(kn=None) == 1                                 # part of the fused store missing
+    assert create(wsb=100) == 3                                 # workspace too small
+    n = lib.pkv_decode_graphs_workspace_bytes(arr, 3, 32, 8, 64, 2048)
+    assert n == max(pkv.pkv_decode_workspace_bytes(b, 32, 8, 64, 2048) for b in (1, 2, 4))
+    used = ctypes.c_int32(7)
+    assert lib.pkv_decode_graphs_replay(None, 1, None, ctypes.byref(used)) == 1
+    assert used.value == 0
+    lib.pkv_decode_graphs_destroy(None)
+
+
 def _multi(**kw):
     a = dict(q=FAKE, L=4, kc=FAKE, vc=FAKE, ps=16, pages=100, pt=FAKE, stride=128, seq=FAKE,
              B=4, maxlen=2048, hq=32, hkv=8, d=64, scale=0.125, split=0, out=FAKE, ws=None,

@@ -149,3 +149,98 @@ def test_prefill_graph_replays_and_counter_resets():
             call()
             torch.cuda.synchronize()
             assert torch.equal(got, out[:w.num_tokens]), "replay differs from the eager call"
+
+
+# ---- graphs per batch-size bucket, padded with the dummy request ----------
+
+BUCKETS = [1, 2, 4, 8, 16, 32, 64]
+GB_MAX, GB_LEN, GB_WIDTH = 64, 1024, 64
+GB_POOL = GB_MAX * GB_WIDTH + 8
+
+
+def _bucket_batch(live, seed):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, GB_LEN + 1, size=live).astype(np.int32)
+    return inputs.build_decode(live, HQ, HKV, D, PS, lens, seed=seed, device="cuda",
+                               pool_pages=GB_POOL, width=GB_WIDTH, store_new=True)
+
+
+@pytest.mark.parametrize("workspace", ["caller", "fixed scratch"])
+def test_decode_graph_buckets_with_padding(workspace):
+    """pkv_decode_graphs_create captures the decode step for buckets
+    1, 2, 4, ..., 64 (largest first) over fixed 64-row buffers; each step
+    copies its batch into the first rows, pads the rest with the dummy request
+    (length 0, the spare page, no slot), and replays the smallest bucket that
+    holds it.  Checked per replay: the bucket chosen, the live rows against
+    the oracle (store, then attention), zeros in the padded rows, rows past
+    the bucket untouched, and the pools bit-exact: only the live requests'
+    new slots change."""
+    dev = "cuda"
+    st = {
+        "q": torch.zeros(GB_MAX, HQ, D, dtype=torch.bfloat16, device=dev),
+        "k_new": torch.zeros(GB_MAX, HKV, D, dtype=torch.bfloat16, device=dev),
+        "v_new": torch.zeros(GB_MAX, HKV, D, dtype=torch.bfloat16, device=dev),
+        "out_loc": torch.full((GB_MAX,), -1, dtype=torch.int32, device=dev),
+        "page_table": torch.zeros(GB_MAX, GB_WIDTH, dtype=torch.int32, device=dev),
+        "seq_lens": torch.zeros(GB_MAX, dtype=torch.int32, device=dev),
+        "k_cache": torch.zeros(GB_POOL + 1, PS, HKV, D, dtype=torch.bfloat16, device=dev),
+        "v_cache": torch.zeros(GB_POOL + 1, PS, HKV, D, dtype=torch.bfloat16, device=dev),
+    }
+    out = torch.zeros(GB_MAX, HQ, D, dtype=torch.bfloat16, device=dev)
+    ws = None
+    if workspace == "caller":
+        nb = pkv.pkv_decode_graphs_workspace_bytes(BUCKETS, HQ, HKV, D, GB_LEN)
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev)
+    scale = 1.0 / np.sqrt(D)
+    graphs = pkv.pkv_decode_graphs_create(
+        BUCKETS, st["q"], st["k_cache"], st["v_cache"], st["page_table"], st["seq_lens"],
+        GB_LEN, scale, out, k_new=st["k_new"], v_new=st["v_new"], out_loc=st["out_loc"],
+        workspace=ws)
+    try:
+        for rep in range(2):
+            for i, live in enumerate([1, 2, 3, 5, 9, 17, 33, 64, 48]):
+                w = _bucket_batch(live, seed=500 + 10 * rep + i)
+                kc, vc = host_pools(w)
+                ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np,
+                                 w.scale)
+                # fixed buffers: the batch in the first rows, the dummy request after
+                for n in ("q", "k_new", "v_new", "out_loc", "page_table", "seq_lens"):
+                    st[n][:live].copy_(getattr(w, n))
+                st["q"][live:].zero_()
+                st["k_new"][live:].zero_()
+                st["v_new"][live:].zero_()
+                st["out_loc"][live:] = -1
+                st["seq_lens"][live:] = 0
+                st["page_table"][live:] = w.poison_page
+                st["k_cache"].copy_(w.k_cache)
+                st["v_cache"].copy_(w.v_cache)
+                out.fill_(5.0)
+                bucket = graphs.replay(live)
+                torch.cuda.synchronize()
+                expect = min(b for b in BUCKETS if b >= live)
+                print(f"graph buckets ({workspace}) rep {rep}: {live} live -> bucket {bucket}",
+                      flush=True)
+                assert bucket == expect
+                got = f64(out)
+                assert_close(got[:live], ref, f"{live} live in bucket {bucket}")
+                assert np.array_equal(got[live:bucket], np.zeros_like(got[live:bucket]))
+                assert (got[bucket:] == 5.0).all(), "rows past the bucket were written"
+                assert np.array_equal(inputs.bf16_bits(st["k_cache"]), kc)
+                assert np.array_equal(inputs.bf16_bits(st["v_cache"]), vc)
+    finally:
+        graphs.destroy()
+
+
+def test_decode_graph_bucket_limits():
+    st = _static_like(_decode_batch(301))
+    out = torch.empty_like(st["q"])
+    graphs = pkv.pkv_decode_graphs_create(
+        [2, 8], st["q"], st["k_cache"], st["v_cache"], st["page_table"], st["seq_lens"],
+        MAX_LEN, 0.125, out, k_new=st["k_new"], v_new=st["v_new"], out_loc=st["out_loc"])
+    try:
+        assert graphs.replay(0) == 0              # nothing to do
+        with pytest.raises(pkv.PKVError):
+            graphs.replay(9)                      # above the largest bucket
+        torch.cuda.synchronize()
+    finally:
+        graphs.destroy()
