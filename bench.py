@@ -191,10 +191,12 @@ def warm_up(step, warmup: int, min_s: float = MIN_WARM_S):
 
 def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
                   fused_store: bool = True, via_prefill: bool = False,
-                  min_warm_s: float = MIN_WARM_S):
+                  min_warm_s: float = MIN_WARM_S, read_once: bool = False):
     """Time one workload's attention call.  A multi-token decode workload runs
     pkv_paged_attn_decode_multi, or with ``via_prefill`` the same batch through
-    pkv_paged_attn_prefill (q_len new tokens after a cached prefix of n - q_len)."""
+    pkv_paged_attn_prefill (q_len new tokens after a cached prefix of n - q_len).
+    ``read_once``: the shared-prefix workload through pkv_paged_attn_decode_shared
+    (one group of all requests, the shared prefix read once per KV head)."""
     import torch
 
     import paged_kv_attention_out_amd as pkv
@@ -221,6 +223,13 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
         ws = torch.zeros(nb, dtype=torch.uint8, device="cuda") if nb else None
     if not is_decode:
         ws = torch.zeros(pkv.pkv_prefill_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    shared_len = inputs.WORKLOADS[name].get("shared_prefix", 0)
+    if read_once:
+        nb = pkv.pkv_paged_attn_decode_shared_workspace_bytes(B, Hq, Hkv, d, w.max_seq_len,
+                                                              shared_len, split_tokens)
+        ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        cu_g = torch.tensor([0, B], dtype=torch.int32, device="cuda")
+        sh_l = torch.full((B,), shared_len, dtype=torch.int32, device="cuda")
     ws_ptr, ws_bytes = (0, 0) if ws is None else (ws.data_ptr(), ws.numel())
 
     # Pre-marshalled C calls: the timed loop only enqueues.
@@ -232,7 +241,14 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
             st = (c.k_new.data_ptr(), c.v_new.data_ptr(), c.out_loc.data_ptr(),
                   c.k_new.shape[0], c.k_cache.data_ptr(), c.v_cache.data_ptr(),
                   c.k_cache.shape[0] * ps, Hkv, d, stream)
-        if is_decode and st is not None and fused_store:
+        if read_once:
+            at = (c.q.data_ptr(), c.k_new.data_ptr(), c.v_new.data_ptr(), c.out_loc.data_ptr(),
+                  c.k_cache.data_ptr(), c.v_cache.data_ptr(), ps, c.num_pages,
+                  c.page_table.data_ptr(), c.page_table.shape[1], c.seq_lens.data_ptr(), B,
+                  w.max_seq_len, cu_g.data_ptr(), sh_l.data_ptr(), 1, B, shared_len, Hq, Hkv,
+                  d, w.scale, split_tokens, out.data_ptr(), ws_ptr, ws_bytes, stream)
+            st = None
+        elif is_decode and st is not None and fused_store:
             # one call: the new rows are written to the pool by the decode kernel
             at = (c.q.data_ptr(), c.k_new.data_ptr(), c.v_new.data_ptr(), c.out_loc.data_ptr(),
                   c.k_cache.data_ptr(), c.v_cache.data_ptr(), ps, c.num_pages,
@@ -259,7 +275,8 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
         calls.append((st, at, out))
     f_store = lib.pkv_store_kv
     fused = is_decode and w.k_new is not None and fused_store
-    f_attn = (lib.pkv_decode_step if fused else
+    f_attn = (lib.pkv_paged_attn_decode_shared if read_once else
+              lib.pkv_decode_step if fused else
               lib.pkv_paged_attn_decode_multi if L > 1 else
               lib.pkv_paged_attn_decode if is_decode else lib.pkv_paged_attn_prefill)
 
@@ -297,7 +314,7 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
         raise RuntimeError(f"{name}: replicas disagree")
     # the split the kernels used: recorded by the split kernel in the last
     # 256-byte slot of the decode workspace (the device may pick a longer one)
-    if is_decode and ws is not None:
+    if is_decode and ws is not None and ws.numel() >= 256:
         split = int(ws[-256:].view(torch.int32)[0].item())
     res = dict(workload=w, replicas=R, split=split, fused=fused,
                ms_per_step=(t1 - t0) * 1e3 / steps,
@@ -476,6 +493,49 @@ def time_metadata(steps: int):
     return res
 
 
+def stream_reference(steps: int):
+    """torch's reduction (read only) and copy kernels over `nbytes` buffers,
+    rotating over replicas so the working set (>= 1 GiB) exceeds the 256 MB
+    Infinity Cache; mean per-call time by HIP events after a 0.25 s warm-up.
+    A reference for the decode kernels' bandwidth, not part of the hot path."""
+    import torch
+
+    from paged_kv_attention_out_amd import inputs
+
+    res = {}
+    w = inputs.make_workload(PRIMARY, device="cpu", poison=False)
+    step_bytes = decode_bytes(w) + store_bytes(w)
+    del w
+    for label, nbytes in (("llama_decode_step_bytes", step_bytes), ("1GiB", 1 << 30)):
+        n = (nbytes // 16) * 4           # float32 elements, a multiple of 4
+        R = max(1, math.ceil(MIN_WORKING_SET / (n * 4)))
+        bufs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(R)]
+        dst = torch.empty_like(bufs[0])
+        out = {}
+        for kind in ("sum", "copy"):
+            def call(i):
+                if kind == "sum":
+                    bufs[i % R].sum()
+                else:
+                    dst.copy_(bufs[i % R])
+            warm_up(call, 5)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for i in range(steps):
+                ev[i][0].record()
+                call(i)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+            moved = n * 4 * (1 if kind == "sum" else 2)
+            out[kind] = {"us_mean": round(us, 2), "bytes": moved,
+                         "GB/s": round(moved / (us * 1e-6) / 1e9, 1)}
+        res[label] = dict(out, replicas=R)
+        del bufs, dst
+        torch.cuda.empty_cache()
+    return res
+
+
 # ---- CPU baseline (the oracle) ------------------------------------------------
 
 def _host_request(w, r):
@@ -594,9 +654,17 @@ def main():
     ap.add_argument("--only", default="", metavar="WORKLOAD",
                     help="only time one named workload (for profiler runs of a single "
                          "kernel), print its timing as JSON and exit")
+    ap.add_argument("--read-once", action="store_true",
+                    help="with --only shared_prefix_decode: time pkv_paged_attn_decode_shared "
+                         "(the shared prefix read once per KV head)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (a known "
                          "byte count for scaling HBM traffic counters) and exit")
+    ap.add_argument("--stream-ref", action="store_true",
+                    help="only time torch's own read kernels (a float32 sum, a device "
+                         "copy) over buffers of the Llama-shaped decode step's size and of "
+                         "1 GiB, rotating over replicas of >= 1 GiB, as a reference for what "
+                         "a plain stream over the same bytes costs, print JSON and exit")
     ap.add_argument("--segment-trace", default=None, metavar="CSV",
                     help="only summarise a rocprofv3 kernel-trace CSV of this script per "
                          "workload (no GPU use) and exit")
@@ -623,8 +691,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": n, "launches": 5}))
         return
+    if args.stream_ref:
+        print(json.dumps(stream_reference(args.steps)))
+        return
     if args.only:
-        r = time_workload(args.only, args.steps, args.warmup, args.split_tokens)
+        r = time_workload(args.only, args.steps, args.warmup, args.split_tokens,
+                          read_once=args.read_once)
         wa = r["workload"]
         rec = {"workload": args.only, "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 2),
                "ms_per_step": round(r["ms_per_step"], 5), "replicas": r["replicas"]}
@@ -701,6 +773,19 @@ def main():
                     ub = unique_kv_bytes(wa)
                     also[name]["unique_kv_bytes"] = ub
                     also[name]["unique_GB/s"] = round(ub / (a["kernel_ms_mean"] * 1e-3) / 1e9, 1)
+                    # the same step with the shared prefix read once per KV head
+                    # (pkv_paged_attn_decode_shared)
+                    torch.cuda.empty_cache()
+                    b = time_workload(name, steps, max(3, args.warmup // 4), read_once=True)
+                    ro_s = b["kernel_ms_mean"] * 1e-3
+                    also[name]["read_once"] = {
+                        "kernel_us_mean": round(b["kernel_ms_mean"] * 1e3, 2),
+                        "ms_per_step": round(b["ms_per_step"], 4),
+                        "GB/s": round(call_b / ro_s / 1e9, 1),
+                        "unique_GB/s": round(ub / ro_s / 1e9, 1),
+                        "unique_frac": round(ub / ro_s / 1e9 / HBM_PEAK_GBS, 4),
+                        "tokens_per_s": round(wa.num_seqs / (b["ms_per_step"] * 1e-3), 1)}
+                    del b
             else:
                 tf = prefill_flops(wa) / (a["kernel_ms_mean"] * 1e-3) / 1e12
                 also[name] = {"TFLOP/s": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4),

@@ -224,6 +224,62 @@ int pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
 size_t pkv_decode_step_noalloc_max_bytes(void);
 
 /*
+ * pkv_paged_attn_decode_shared -- decode (or the decode step, with the new
+ * token's store) for a batch whose requests share cached prefixes, reading
+ * each shared prefix once for all requests that share it.
+ *
+ * With prefix caching, requests that start with the same tokens point their
+ * first page-table entries at the same physical pages (miniVLLM "Engine
+ * Architecture", prepare_prefill: block tables for prefix reuse;
+ * zero-to-sglang Ch.1, section 4 roadmap: RadixAttention).  The result is
+ * that of pkv_paged_attn_decode (pkv_decode_step when k_new, v_new and
+ * out_loc are given), up to rounding.  The work is split in two passes on
+ * `stream`: for every group, the queries of all its members (all query
+ * heads of a KV head) against the group's shared prefix as one MFMA
+ * product per 64-key split of the prefix; then every request's remaining
+ * tokens as in pkv_paged_attn_decode; the partial results of both are
+ * merged by the split-merge kernel.
+ *
+ *   cu_groups    : [num_groups + 1] int32, cu_groups[0] = 0, non-decreasing,
+ *                  cu_groups[num_groups] = num_seqs: group g is requests
+ *                  cu_groups[g] .. cu_groups[g+1]-1 (a group of one request,
+ *                  or with shared length 0, shares nothing)
+ *   shared_lens  : [num_seqs] int32, tokens at the start of request r's
+ *                  context that it shares with its group; used rounded down
+ *                  to a multiple of 16.  Preconditions (not checked): every
+ *                  member of a group has the same shared length and the same
+ *                  page-table entries for it (the pass reads the pages through
+ *                  the group's first member), and 0 <= shared_lens[r] <=
+ *                  seq_lens[r] (< seq_lens[r] with the store: the new token
+ *                  lies after the shared prefix).
+ *   num_groups   : 1 .. num_seqs
+ *   max_group_size, max_shared_len : host upper bounds (size the launch);
+ *                  max_shared_len <= max_seq_len
+ *   k_new, v_new, out_loc : as pkv_decode_step, or all NULL for plain decode
+ *   workspace    : at least pkv_paged_attn_decode_shared_workspace_bytes(...)
+ *                  bytes, 256-byte aligned (contents on entry do not matter)
+ *   all others   : as pkv_decode_step
+ *
+ * Errors as pkv_decode_step; bad group arguments -> PKV_EINVAL.
+ */
+int pkv_paged_attn_decode_shared(const void* q, const void* k_new, const void* v_new,
+                                 const int32_t* out_loc, void* k_cache, void* v_cache,
+                                 int32_t page_size, int64_t num_pages,
+                                 const int32_t* page_table, int32_t page_table_stride,
+                                 const int32_t* seq_lens, int32_t num_seqs,
+                                 int32_t max_seq_len, const int32_t* cu_groups,
+                                 const int32_t* shared_lens, int32_t num_groups,
+                                 int32_t max_group_size, int32_t max_shared_len,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 float softmax_scale, int32_t split_tokens, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+size_t pkv_paged_attn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_seq_len, int32_t max_shared_len,
+                                                    int32_t split_tokens);
+
+/*
  * Decode-step graphs, one per batch-size bucket.
  *
  * The engines capture the decode step in graphs for a set of batch sizes

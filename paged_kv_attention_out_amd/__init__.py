@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
     pkv_decode_workspace_bytes,
     pkv_paged_attn_decode,
     pkv_paged_attn_decode_multi,
+    pkv_paged_attn_decode_shared,
+    pkv_paged_attn_decode_shared_workspace_bytes,
     pkv_paged_attn_prefill,
     pkv_prefill_metadata,
     pkv_prefill_workspace_bytes,

@@ -50,6 +50,12 @@ SIGNATURES = {
         _c_void_p, _i32, _c_void_p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p,
         _c_void_p]),
     "pkv_decode_step_noalloc_max_bytes": (_size, []),
+    "pkv_paged_attn_decode_shared": (ctypes.c_int, [
+        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64,
+        _c_void_p, _i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32,
+        _i32, _i32, _f32, _i32, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "pkv_paged_attn_decode_shared_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                             _i32]),
     "pkv_decode_graphs_workspace_bytes": (_size, [_c_void_p, _i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_graphs_create": (ctypes.c_int, [
         _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -293,6 +299,65 @@ def pkv_decode_step_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
 
 def pkv_decode_step_noalloc_max_bytes() -> int:
     return int(lib().pkv_decode_step_noalloc_max_bytes())
+
+
+def pkv_paged_attn_decode_shared_workspace_bytes(num_seqs: int, num_q_heads: int,
+                                                 num_kv_heads: int, head_dim: int,
+                                                 max_seq_len: int, max_shared_len: int,
+                                                 split_tokens: int = 0) -> int:
+    return int(lib().pkv_paged_attn_decode_shared_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, max_shared_len,
+        split_tokens))
+
+
+def pkv_paged_attn_decode_shared(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 page_table: torch.Tensor, seq_lens: torch.Tensor,
+                                 max_seq_len: int, cu_groups: torch.Tensor,
+                                 shared_lens: torch.Tensor, max_group_size: int,
+                                 max_shared_len: int, softmax_scale: float,
+                                 out: Optional[torch.Tensor] = None,
+                                 k_new: Optional[torch.Tensor] = None,
+                                 v_new: Optional[torch.Tensor] = None,
+                                 out_loc: Optional[torch.Tensor] = None,
+                                 workspace: Optional[torch.Tensor] = None,
+                                 split_tokens: int = 0) -> torch.Tensor:
+    """Decode (with the new token's store when k_new/v_new/out_loc are
+    given) over requests grouped by shared prefix: group g is requests
+    cu_groups[g] .. cu_groups[g+1]-1, sharing their first shared_lens tokens."""
+    B, hkv, d = _check_decode_shapes(q, k_cache, v_cache, page_table, seq_lens, out, workspace)
+    _shape(cu_groups, (None,), "cu_groups")
+    if cu_groups.numel() < 2:
+        raise ValueError("cu_groups needs at least two entries")
+    _numel(shared_lens, B, "shared_lens")
+    if k_new is not None:
+        _shape(k_new, (B, hkv, d), "k_new")
+        _shape(v_new, (B, hkv, d), "v_new")
+        _numel(out_loc, B, "out_loc")
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            _dev(t, torch.bfloat16, name)
+        _dev(out_loc, torch.int32, "out_loc")
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, torch.bfloat16, name)
+    for t, name in ((page_table, "page_table"), (seq_lens, "seq_lens"), (cu_groups, "cu_groups"),
+                    (shared_lens, "shared_lens")):
+        _dev(t, torch.int32, name)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out")
+    if workspace is None:
+        nbytes = pkv_paged_attn_decode_shared_workspace_bytes(
+            B, q.shape[1], hkv, d, max_seq_len, max_shared_len, split_tokens)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    num_pages, ps = k_cache.shape[0], k_cache.shape[1]
+    _check(lib().pkv_paged_attn_decode_shared(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out_loc), _ptr(k_cache), _ptr(v_cache), ps,
+        num_pages, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, max_seq_len,
+        _ptr(cu_groups), _ptr(shared_lens), cu_groups.numel() - 1, max_group_size,
+        max_shared_len, q.shape[1], hkv, d, softmax_scale, split_tokens, _ptr(out),
+        _ptr(workspace), ws_bytes, _stream(q)), "pkv_paged_attn_decode_shared")
+    return out
 
 
 def _buckets(buckets):

@@ -33,9 +33,11 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <new>
 
 #include "pkv_common.h"
+#include "prefix_pass.h"
 
 #ifndef PKV_DECODE_NBUF_D64
 #define PKV_DECODE_NBUF_D64 8
@@ -77,14 +79,32 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t max_seq_len;
   int32_t split;        // host split (tokens); the device may pick a longer one
-  int32_t n_split_max;  // splits per request at the host split (sizes grid and workspace)
+  int32_t n_split_max;  // partial slots per (request, KV head): shared-prefix splits (if
+                        // any), then the splits per request at the host split
+  int32_t n_unit_splits;  // splits per request at the host split (sizes the grid)
   int32_t round_units;  // units per KV head and query slice that one round of resident
                         // waves holds; 0 = use `split` as given
   int32_t q_len;     // query tokens per request (1 for plain decode)
   int32_t q_slices;  // units per (request, KV head, split): each takes LQ query tokens
   int32_t heads_per_block;  // waves per workgroup, one per KV head (1, 2, 4 or 8)
   float scale_log2;  // softmax_scale * log2(e)
+  // Shared prefixes (pkv_paged_attn_decode_shared): request r's first
+  // skip[r] tokens (rounded down to 16) are attended by the shared-prefix
+  // pass, whose partials fill slots 0 .. ceil(skip / ksplit) - 1 of (r, KV
+  // head); the splits here cover the rest of the context and take the slots
+  // after them.  Null: no request skips anything.
+  const int32_t* skip;
+  int32_t ksplit;
 };
+
+// Tokens of request r attended by the shared-prefix pass (0 without one),
+// a multiple of 16 not above n, and the partial slots that pass fills.
+__device__ __forceinline__ int skip_tokens(const DecodeParams& p, int skip_raw, int n) {
+  return p.skip == nullptr ? 0 : min(max(skip_raw, 0), max(n, 0)) & ~15;
+}
+__device__ __forceinline__ int prefix_slots(const DecodeParams& p, int skip) {
+  return skip == 0 ? 0 : (skip + p.ksplit - 1) / p.ksplit;
+}
 
 constexpr float kTau = 8.0f;
 
@@ -243,8 +263,11 @@ struct DecodeTraits {
 //   column 4*(L%4) gives every lane 4 consecutive keys of one dim.
 //   O (16 head rows x D dims) lives in D/16 accumulators of 4 registers;
 //   row 4c+i is query head i % G.
-template <int D, int G, int LQ>
-__global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
+// SKIP: requests may skip their shared-prefix tokens (p.skip); compiled
+// out of the kernels of plain decode.
+template <int D, int G, int LQ, bool SKIP>
+__device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const uint32_t bid,
+                                                  uint16_t* vlds_block) {
   constexpr int KCH = D / 32;  // 16-byte pieces per lane per row == QK MFMAs per group
   constexpr int NT = D / 16;   // 16-dim tiles of the output == PV MFMAs per pair
   constexpr int NBUF = DecodeTraits<D, G>::NBUF;
@@ -253,7 +276,6 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "query heads per KV head");
   static_assert(NC <= 16 && (16 % NC) == 0, "the 16 MFMA columns hold whole copies of the columns");
   // LDS: NBUF * 16 * VPITCH values per wave, sized at launch.
-  extern __shared__ __attribute__((aligned(16))) uint16_t vlds_block[];
   // A workgroup holds heads_per_block waves, one per KV head of the same
   // unit: adjacent heads' slices of every token row are then read by one
   // CU at the same time.
@@ -274,45 +296,64 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   // with that a multiple of 8 they share an XCD, so the second slice reads
   // K/V from L2.
   const uint32_t hblocks = (uint32_t)(p.num_kv_heads / p.heads_per_block);  // blocks per unit
-  const uint32_t u = blockIdx.x / hblocks;
+  const uint32_t u = bid / hblocks;
   const uint32_t rank = LQ == 1 ? u : u / (uint32_t)p.q_slices;
   const int tq0 = LQ == 1 ? 0 : (int)(u % (uint32_t)p.q_slices) * LQ;  // first query token
   const int QL = LQ == 1 ? 1 : p.q_len;
-  const int kvh = (int)((blockIdx.x + rank) % hblocks) * p.heads_per_block + wv;
+  const int kvh = (int)((bid + rank) % hblocks) * p.heads_per_block + wv;
   // The first 256 request lengths: four loads at clamped indices, issued
   // together (one memory round trip; the empty asm keeps the compiler from
   // moving each load into a branch of its own).  Then, not waited for with
   // them, one 256-byte piece of the page table per wave: the waves of an
   // XCD together bring the rows of a small table into its L2 while the unit
   // is being found, so the window read below hits there.
+  // With shared prefixes a request's work is the rest of its context after
+  // the skipped tokens; a request whose whole context is shared has no unit
+  // here (-1, as a missing request).
   Lens4 lens;
+  int skv[4] = {0, 0, 0, 0};
   int pf;
   {
-    int x[4];
+    int x[4], y[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[k] = p.seq_lens[min(64 * k + lane, p.num_seqs - 1)];
+    if (SKIP) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[k] = p.skip[min(64 * k + lane, p.num_seqs - 1)];
+    }
     const int64_t pt_entries = (int64_t)p.num_seqs * p.pt_stride;
-    pf = p.page_table[min(((int64_t)(blockIdx.x >> 3) * p.heads_per_block + wv) * 64 + lane,
+    pf = p.page_table[min(((int64_t)(bid >> 3) * p.heads_per_block + wv) * 64 + lane,
                           pt_entries - 1)];
     asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      lens.v[k] = 64 * k + lane < p.num_seqs ? min(max(x[k], 0), p.max_seq_len) : -1;
+    for (int k = 0; k < 4; ++k) {
+      const int n = min(max(x[k], 0), p.max_seq_len);
+      skv[k] = SKIP ? skip_tokens(p, y[k], n) : 0;
+      const int w = n - skv[k];
+      lens.v[k] = 64 * k + lane < p.num_seqs && (skv[k] == 0 || w > 0) ? w : -1;
+    }
   }
   const int sl = device_split(p, lens);  // tokens per split
-  if (p.ws_split != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *p.ws_split = sl;
-  int r = -1, split = 0, n = 0;
+  if (p.ws_split != nullptr && bid == 0 && threadIdx.x == 0) *p.ws_split = sl;
+  int r = -1, split = 0, n = 0, skip = 0;  // n: work tokens after the skipped ones
   {
     // Units in two parts: first every full-length split of every request
     // (request-major), then the short last split of each request whose
     // length is not a multiple of the split (and the one unit of an empty
     // request), so that the grid ends with its shortest units and the last
     // round of a multi-round launch drains quickly.
-    auto chunk_len = [&](int c0) -> int {  // -1: no request
+    int chunk_skip = 0;  // this lane's skipped tokens in the current chunk
+    auto chunk_len = [&](int c0) -> int {  // work tokens; -1: no request (or no work)
       const int k = c0 >> 6;
-      if (k < 4) return k == 0 ? lens.v[0] : k == 1 ? lens.v[1] : k == 2 ? lens.v[2] : lens.v[3];
+      if (k < 4) {
+        chunk_skip = k == 0 ? skv[0] : k == 1 ? skv[1] : k == 2 ? skv[2] : skv[3];
+        return k == 0 ? lens.v[0] : k == 1 ? lens.v[1] : k == 2 ? lens.v[2] : lens.v[3];
+      }
       const int rr = c0 + lane;
-      return rr < p.num_seqs ? min(max(p.seq_lens[rr], 0), p.max_seq_len) : -1;
+      if (rr >= p.num_seqs) return -1;
+      const int n = min(max(p.seq_lens[rr], 0), p.max_seq_len);
+      chunk_skip = SKIP ? skip_tokens(p, p.skip[rr], n) : 0;
+      return chunk_skip == 0 || n > chunk_skip ? n - chunk_skip : -1;
     };
     int target = (int)rank;
     for (int part = 0; part < 2 && r < 0; ++part) {
@@ -332,6 +373,7 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
           split = part == 0 ? rel - __builtin_amdgcn_readlane(inc - cnt, lr)
                             : __builtin_amdgcn_readlane(full, lr);
           n = __builtin_amdgcn_readlane(len, lr);
+          skip = SKIP ? __builtin_amdgcn_readlane(chunk_skip, lr) : 0;
           break;
         }
         base += total;
@@ -341,6 +383,7 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   }
   if (r < 0) return;  // past the last pair
   const int64_t rk = (int64_t)r * p.num_kv_heads + kvh;
+  const int slot0 = prefix_slots(p, skip);  // partial slots of the shared-prefix pass
   const int j = lane & 15;  // token within the group / score column
   const int c = lane >> 4;  // 16-byte piece within each 64-byte block / token quad
   const int col = j % NC;   // logical column of this lane: query token col / G, head col % G
@@ -348,7 +391,7 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   // Query token of the column; columns past the last token repeat it and
   // are never written.
   const int tq = min(tq0 + col / G, QL - 1);
-  const int t_begin = split * sl;
+  const int t_begin = skip + split * sl;
 
   // Q^T fragments (B operand): column j holds query token tq of head
   // kvh*G + hcol (the NC columns repeat over the 16 MFMA columns).
@@ -388,7 +431,10 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
     return;
   }
   const int ns = (n + sl - 1) / sl;
-  const int t_end = min(n, t_begin + sl);
+  const int t_end = min(skip + n, t_begin + sl);
+  // The output is written directly only when this split is the request's
+  // one partial; otherwise partials go to the workspace.
+  const bool direct = ns == 1 && slot0 == 0;
 
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
   // Fused step: the request's last split writes this head's slice of the
@@ -414,7 +460,7 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
 
   // Fused step: the lane whose token is the new one (position n - 1) reads
   // its row from k_new / v_new instead of the pool.
-  const int t_new = LQ == 1 && p.k_new != nullptr ? n - 1 : -1;
+  const int t_new = LQ == 1 && p.k_new != nullptr ? skip + n - 1 : -1;
   const int64_t new_off = ((int64_t)r * p.num_kv_heads + kvh) * D + 8 * c;
 
   uint4 kb[NBUF][KCH], vb[NBUF][KCH];
@@ -470,8 +516,8 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
   float l_own = 0.f;      // this lane's share of the row sum of its column
   // Query token tq sits at position n - QL + tq and sees keys up to there;
   // lim_lo is the lowest limit among this block's columns.
-  const int lim = n - QL + tq;
-  const int lim_lo = n - QL + tq0;
+  const int lim = skip + n - QL + tq;
+  const int lim_lo = skip + n - QL + tq0;
 
   const int trq = j & 3, trj = j >> 2;  // transpose-read lane roles
 
@@ -614,7 +660,7 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
     const float Mx = __shfl(m_own, x % NC);
     const int h = x % G, tx = tq0 + x / G;
     if (x >= NC || tx >= QL) continue;
-    if (ns == 1) {
+    if (direct) {
       // (a multi-token row with no visible key has L = 0 and gets zeros)
       const float inv = LQ > 1 && Lx == 0.f ? 0.f : 1.f / Lx;
       uint16_t* o_row =
@@ -624,7 +670,7 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
     } else {
       // Partial (m, l, un-normalised o) of this split for column (tx, h)
       // among the QL * G columns of the request's KV head.
-      const int64_t base = (rk * p.n_split_max + split) * (QL * G) + tx * G + h;
+      const int64_t base = (rk * p.n_split_max + slot0 + split) * (QL * G) + tx * G + h;
       float* dst = p.ws_o + base * D + dl;
 #pragma unroll
       for (int t = 0; t < NT; ++t) dst[16 * t] = o[t][i];
@@ -634,6 +680,36 @@ __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(Dec
       }
     }
   }
+}
+
+template <int D, int G, int LQ, bool SKIP = false>
+__global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t vlds_block[];
+  decode_split_unit<D, G, LQ, SKIP>(p, blockIdx.x, vlds_block);
+}
+
+// The split kernel for batches with shared prefixes: the grid's first
+// x.items workgroups run the shared-prefix pass (one item each), the rest
+// the units of each request's remaining tokens, four KV heads per
+// workgroup.  Both kinds are in flight together, and their partials go to
+// disjoint slots of the workspace.
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void decode_split_prefix_kernel(DecodeParams p,
+                                                                     pkv_prefix::Params x) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_block[];
+  if (blockIdx.x < (uint32_t)x.items) {
+    pkv_prefix::prefix_item<D, D == 64 ? 2 : 1, G>(x, blockIdx.x, lds_block, (int)threadIdx.x);
+    return;
+  }
+  decode_split_unit<D, G, 1, true>(p, blockIdx.x - (uint32_t)x.items, lds_block);
+}
+
+// The shared-prefix pass alone (for KV head counts the combined kernel's
+// four-head workgroups do not fit), before the split kernel on one stream.
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void prefix_pass_kernel(pkv_prefix::Params x) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_block[];
+  pkv_prefix::prefix_item<D, D == 64 ? 2 : 1, G>(x, blockIdx.x, lds_block, (int)threadIdx.x);
 }
 
 // The loads of a batch of splits do not depend on the request length: the
@@ -665,6 +741,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const float* oo = p.ws_o + (sbase * NC + x) * D + lane;
 
   int n = p.seq_lens[r];
+  int skip_raw = p.skip != nullptr ? p.skip[r] : 0;
   // First batch of partials, issued together with the length.  With a
   // device-chosen split the units fit one round, so requests have few
   // splits: only 8 are fetched ahead (the bound nsm, from the host split,
@@ -681,9 +758,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   n = uniform(n);
   n = n > p.max_seq_len ? p.max_seq_len : n;
   if (n <= 0) return;
+  const int skip = skip_tokens(p, uniform(skip_raw), n);
   const int sl = p.round_units > 0 ? uniform(*p.ws_split) : p.split;  // as the split kernel used
-  const int ns = (n + sl - 1) / sl;
-  if (ns == 1) return;  // written by the split kernel
+  // partials: those of the shared-prefix pass, then one per split of the rest
+  const int ns = prefix_slots(p, skip) + (n - skip + sl - 1) / sl;
+  if (ns == 1 && skip == 0) return;  // written by the split kernel
 
   // Global max over the splits (lane s holds split s, 64 at a time).
   float M = kNegInf;
@@ -818,8 +897,38 @@ int resident_waves(int hpb) {
   return n;
 }
 
+// Resident waves of decode_split_prefix_kernel<D, G> (four-wave workgroups)
+// on the current device, cached per device.
+template <int D, int G>
+int resident_waves_shared() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  constexpr size_t kWaveLds = (size_t)DecodeTraits<D, G>::NBUF * 16 * (D + 8) * sizeof(uint16_t);
+  const size_t lds = std::max(kWaveLds * 4, pkv_prefix::item_lds_bytes<D>());
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(decode_split_prefix_kernel<D, G>), 256, lds) !=
+      hipSuccess)
+    return 0;
+  const int n = cus * per_cu * 4;
+  if (n > 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// With `x` (a shared-prefix pass, single-token queries, Hkv a multiple of
+// four) the split kernel is decode_split_prefix_kernel: x->items workgroups
+// of the pass ahead of the units, four KV heads per workgroup.
 template <int D, int G, int LQ>
-int launch_decode(DecodeParams p, int64_t waves, hipStream_t s) {
+int launch_decode(DecodeParams p, int64_t waves, hipStream_t s,
+                  const pkv_prefix::Params* x = nullptr) {
   constexpr size_t kWaveLds = (size_t)DecodeTraits<D, G>::NBUF * 16 * (D + 8) * sizeof(uint16_t);
   // KV heads per workgroup: adjacent heads' slices of every token row are
   // read by one CU at the same time.  Four when Hkv allows; eight when one
@@ -827,6 +936,7 @@ int launch_decode(DecodeParams p, int64_t waves, hipStream_t s) {
   // CU, so none is held back by a slow wave of a large workgroup), while
   // with several rounds eight per workgroup is slower than four.
   const int hkv = p.num_kv_heads;
+  const bool shared = LQ == 1 && x != nullptr;
   int hpb = hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1;
   int64_t blocks = waves / hpb;
   if (p.round_units < 0) {
@@ -834,10 +944,11 @@ int launch_decode(DecodeParams p, int64_t waves, hipStream_t s) {
     // holds.  Use the device's split choice only when even max-length
     // requests need at most 4 rounds at the host split; then one round of
     // workgroups covers every unit it can produce.
-    const int hpb1 = hkv % 8 == 0 ? 8 : hpb;
+    const int hpb1 = hkv % 8 == 0 && !shared ? 8 : hpb;
     const int64_t per_unit = (int64_t)hkv * (LQ == 1 ? 1 : p.q_slices);
-    const int64_t T = resident_waves<D, G, LQ>(hpb1) / per_unit;
-    const int64_t worst = (int64_t)p.num_seqs * p.n_split_max;  // units per head at the host split
+    const int64_t T =
+        (shared ? resident_waves_shared<D, G>() : resident_waves<D, G, LQ>(hpb1)) / per_unit;
+    const int64_t worst = (int64_t)p.num_seqs * p.n_unit_splits;  // units per head, host split
     if (T > 0 && p.num_seqs <= T && worst <= 4 * T) {
       p.round_units = (int32_t)T;
       hpb = hpb1;
@@ -848,9 +959,30 @@ int launch_decode(DecodeParams p, int64_t waves, hipStream_t s) {
   }
   if (blocks > INT32_MAX) return PKV_EINVAL;
   p.heads_per_block = hpb;
-  const int st = pkv_host::launch(decode_split_kernel<D, G, LQ>, dim3((unsigned)blocks),
-                                  dim3(64 * p.heads_per_block), s, p,
-                                  kWaveLds * p.heads_per_block);
+  int st;
+  if constexpr (LQ == 1) {
+    if (shared) {
+      if (hpb != 4 || blocks + x->items > INT32_MAX) return PKV_EINVAL;
+      const size_t lds = std::max(kWaveLds * 4, pkv_prefix::item_lds_bytes<D>());
+      DecodeParams pp = p;
+      pkv_prefix::Params xx = *x;
+      void* args[] = {&pp, &xx};
+      st = hipLaunchKernel(reinterpret_cast<const void*>(decode_split_prefix_kernel<D, G>),
+                           dim3((unsigned)(blocks + x->items)), dim3(256), args, lds, s) ==
+                   hipSuccess
+               ? PKV_OK
+               : PKV_EHIP;
+    } else if (p.skip != nullptr) {
+      st = pkv_host::launch(decode_split_kernel<D, G, 1, true>, dim3((unsigned)blocks),
+                            dim3(64 * p.heads_per_block), s, p, kWaveLds * p.heads_per_block);
+    } else {
+      st = pkv_host::launch(decode_split_kernel<D, G, LQ>, dim3((unsigned)blocks),
+                            dim3(64 * p.heads_per_block), s, p, kWaveLds * p.heads_per_block);
+    }
+  } else {
+    st = pkv_host::launch(decode_split_kernel<D, G, LQ>, dim3((unsigned)blocks),
+                          dim3(64 * p.heads_per_block), s, p, kWaveLds * p.heads_per_block);
+  }
   if (st != PKV_OK || p.n_split_max <= 1) return st;
   const int64_t cblocks = ((int64_t)p.num_seqs * p.q_len * p.num_q_heads + 3) / 4;
   return pkv_host::launch(decode_combine_kernel<D, G>, dim3((unsigned)cblocks), dim3(256), s,
@@ -858,9 +990,10 @@ int launch_decode(DecodeParams p, int64_t waves, hipStream_t s) {
 }
 
 template <int D, int G>
-int launch_decode_lq(const DecodeParams& p, int lq, int64_t waves, hipStream_t s) {
+int launch_decode_lq(const DecodeParams& p, int lq, int64_t waves, hipStream_t s,
+                     const pkv_prefix::Params* x = nullptr) {
   switch (lq) {
-    case 1: return launch_decode<D, G, 1>(p, waves, s);
+    case 1: return launch_decode<D, G, 1>(p, waves, s, x);
     case 2: return launch_decode<D, G, 2>(p, waves, s);
     case 4:
       if constexpr (G <= 4) return launch_decode<D, G, 4>(p, waves, s);
@@ -946,6 +1079,39 @@ void* scratch_on_current_device() {
 
 namespace {
 
+// Requests grouped by shared cached prefix (pkv_paged_attn_decode_shared).
+struct SharedGroups {
+  const int32_t* cu_groups;    // [num_groups + 1]
+  const int32_t* shared_lens;  // [num_seqs]
+  int32_t num_groups;
+  int32_t max_group_size;
+  int32_t max_shared_len;
+};
+
+template <int D, int G>
+int launch_prefix_kernel(const pkv_prefix::Params& x, hipStream_t s) {
+  pkv_prefix::Params xx = x;
+  void* args[] = {&xx};
+  return hipLaunchKernel(reinterpret_cast<const void*>(prefix_pass_kernel<D, G>),
+                         dim3((unsigned)x.items), dim3(256), args,
+                         pkv_prefix::item_lds_bytes<D>(), s) == hipSuccess
+             ? PKV_OK
+             : PKV_EHIP;
+}
+
+int launch_prefix_pass(const pkv_prefix::Params& x, int head_dim, int g, hipStream_t s) {
+  if (head_dim == 64) {
+    if (g == 1) return launch_prefix_kernel<64, 1>(x, s);
+    if (g == 2) return launch_prefix_kernel<64, 2>(x, s);
+    if (g == 4) return launch_prefix_kernel<64, 4>(x, s);
+    return launch_prefix_kernel<64, 8>(x, s);
+  }
+  if (g == 1) return launch_prefix_kernel<128, 1>(x, s);
+  if (g == 2) return launch_prefix_kernel<128, 2>(x, s);
+  if (g == 4) return launch_prefix_kernel<128, 4>(x, s);
+  return launch_prefix_kernel<128, 8>(x, s);
+}
+
 int decode_impl(const void* q, const void* k_new, const void* v_new, const int32_t* out_loc,
                 const void* k_cache, const void* v_cache, int32_t page_size, int64_t num_pages,
                 const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
@@ -953,7 +1119,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
                 int32_t num_kv_heads,
                 int32_t head_dim, float softmax_scale, int32_t split_tokens, void* out,
                 void* workspace, size_t workspace_bytes, void* stream,
-                bool use_scratch = false) {
+                bool use_scratch = false, const SharedGroups* groups = nullptr) {
   using namespace pkv_host;
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                        split_tokens))
@@ -977,12 +1143,17 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
 
   const int32_t split = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
   const int64_t nsm = (max_seq_len + split - 1) / split;
+  // partial slots of the shared-prefix pass, ahead of the splits
+  const int64_t nks = groups == nullptr ? 0
+                                        : ((int64_t)(groups->max_shared_len & ~15) +
+                                           pkv_prefix::kSplit - 1) / pkv_prefix::kSplit;
+  const int64_t slots = nks + nsm;
   const int64_t rk = (int64_t)num_seqs * num_kv_heads;
   const int lq = query_tile(q_len, g);
   const int slices = (q_len + lq - 1) / lq;
   DecodeParams p = {};
-  if (nsm > 1) {
-    const WsLayout w = ws_layout(rk, nsm, (int64_t)g * q_len, head_dim);
+  if (slots > 1) {
+    const WsLayout w = ws_layout(rk, slots, (int64_t)g * q_len, head_dim);
     if (use_scratch) {  // the library's fixed scratch instead of a caller workspace
       workspace_bytes = kScratchBytes;
       if (workspace_bytes < w.total) return PKV_ENOSPACE;
@@ -1023,7 +1194,8 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   p.num_kv_heads = num_kv_heads;
   p.max_seq_len = max_seq_len;
   p.split = split;
-  p.n_split_max = (int32_t)nsm;
+  p.n_split_max = (int32_t)slots;
+  p.n_unit_splits = (int32_t)nsm;
   // Device-chosen split (see device_split): only for the automatic split and
   // batches that need few rounds even at the longest length.
   p.round_units = split_tokens == 0 && num_seqs <= 256 ? -1 : 0;
@@ -1031,16 +1203,69 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   p.q_slices = slices;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (head_dim == 64) {
-    if (g == 1) return launch_decode_lq<64, 1>(p, lq, waves, s);
-    if (g == 2) return launch_decode_lq<64, 2>(p, lq, waves, s);
-    if (g == 4) return launch_decode_lq<64, 4>(p, lq, waves, s);
-    return launch_decode_lq<64, 8>(p, lq, waves, s);
+  pkv_prefix::Params x = {};
+  const pkv_prefix::Params* xp = nullptr;
+  if (groups != nullptr) {
+    // The shared-prefix pass fills slots 0 .. nks-1; the units of each
+    // request's remaining tokens the slots after them.  With four or more
+    // KV heads (a multiple of four) both run in one launch of the combined
+    // split kernel, else the pass runs first as a kernel of its own.  (The
+    // pass alone on a second stream, forked and joined with events,
+    // measured slower than one stream: 51.8 against 37.7 us on the
+    // shared-prefix batch.)
+    p.skip = groups->shared_lens;
+    p.ksplit = pkv_prefix::kSplit;
+    if (nks > 0) {
+      const int nb = head_dim == 64 ? 2 : 1;
+      const int qtile = 128 * nb / g;
+      const int64_t page_bytes = (int64_t)page_size * num_kv_heads * head_dim * 2;
+      if (page_bytes >= ((int64_t)1 << 32)) return PKV_EUNSUPPORTED;
+      x.q = p.q;
+      x.cu_groups = groups->cu_groups;
+      x.shared_lens = groups->shared_lens;
+      x.k_cache = p.k_cache;
+      x.v_cache = p.v_cache;
+      x.page_table = page_table;
+      x.ws_m = p.ws_m;
+      x.ws_l = p.ws_l;
+      x.ws_o = p.ws_o;
+      x.num_groups = groups->num_groups;
+      x.num_seqs = num_seqs;
+      x.max_group_size = groups->max_group_size;
+      x.max_shared_len = groups->max_shared_len;
+      x.page_size = page_size;
+      x.page_shift = p.page_shift;
+      x.pt_stride = page_table_stride;
+      x.num_q_heads = num_q_heads;
+      x.num_kv_heads = num_kv_heads;
+      x.n_qtiles = (groups->max_group_size + qtile - 1) / qtile;
+      x.ksplit = pkv_prefix::kSplit;
+      x.slots = (int32_t)slots;
+      const int64_t items = nks * x.n_qtiles * (int64_t)groups->num_groups * num_kv_heads;
+      if (items > INT32_MAX / 2) return PKV_EINVAL;
+      x.items = (int32_t)items;
+      x.num_pages_u32 = (uint32_t)std::min<int64_t>(num_pages, INT32_MAX);
+      x.page_bytes = (uint32_t)page_bytes;
+      x.row_bytes = (uint32_t)(num_kv_heads * head_dim * 2);
+      x.scale_log2 = p.scale_log2;
+      if (num_kv_heads % 4 == 0) {
+        xp = &x;
+      } else if (x.items > 0) {
+        const int st = launch_prefix_pass(x, head_dim, g, s);
+        if (st != PKV_OK) return st;
+      }
+    }
   }
-  if (g == 1) return launch_decode_lq<128, 1>(p, lq, waves, s);
-  if (g == 2) return launch_decode_lq<128, 2>(p, lq, waves, s);
-  if (g == 4) return launch_decode_lq<128, 4>(p, lq, waves, s);
-  return launch_decode_lq<128, 8>(p, lq, waves, s);
+  if (head_dim == 64) {
+    if (g == 1) return launch_decode_lq<64, 1>(p, lq, waves, s, xp);
+    if (g == 2) return launch_decode_lq<64, 2>(p, lq, waves, s, xp);
+    if (g == 4) return launch_decode_lq<64, 4>(p, lq, waves, s, xp);
+    return launch_decode_lq<64, 8>(p, lq, waves, s, xp);
+  }
+  if (g == 1) return launch_decode_lq<128, 1>(p, lq, waves, s, xp);
+  if (g == 2) return launch_decode_lq<128, 2>(p, lq, waves, s, xp);
+  if (g == 4) return launch_decode_lq<128, 4>(p, lq, waves, s, xp);
+  return launch_decode_lq<128, 8>(p, lq, waves, s, xp);
 }
 
 }  // namespace
@@ -1274,3 +1499,42 @@ extern "C" int pkv_decode_graphs_replay(pkv_decode_graphs* graphs, int32_t num_s
 }
 
 extern "C" void pkv_decode_graphs_destroy(pkv_decode_graphs* graphs) { destroy_graphs(graphs); }
+
+// ---- decode with shared prefixes read once per group ---------------------------
+
+extern "C" size_t pkv_paged_attn_decode_shared_workspace_bytes(
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_seq_len, int32_t max_shared_len, int32_t split_tokens) {
+  if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                       split_tokens) ||
+      num_seqs == 0 || max_shared_len < 0 || max_shared_len > max_seq_len)
+    return 0;
+  const int32_t s = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
+  const int64_t slots = ((int64_t)(max_shared_len & ~15) + pkv_prefix::kSplit - 1) /
+                            pkv_prefix::kSplit +
+                        (max_seq_len + s - 1) / s;
+  if (slots <= 1) return 0;
+  return ws_layout((int64_t)num_seqs * num_kv_heads, slots, num_q_heads / num_kv_heads, head_dim)
+      .total;
+}
+
+extern "C" int pkv_paged_attn_decode_shared(
+    const void* q, const void* k_new, const void* v_new, const int32_t* out_loc, void* k_cache,
+    void* v_cache, int32_t page_size, int64_t num_pages, const int32_t* page_table,
+    int32_t page_table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+    const int32_t* cu_groups, const int32_t* shared_lens, int32_t num_groups,
+    int32_t max_group_size, int32_t max_shared_len, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float softmax_scale, int32_t split_tokens, void* out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!cu_groups || !shared_lens)) return PKV_EINVAL;
+  if (num_groups < 0 || (num_seqs > 0 && num_groups == 0) || num_groups > num_seqs)
+    return PKV_EINVAL;
+  if (max_group_size < 0 || max_group_size > num_seqs) return PKV_EINVAL;
+  if (max_shared_len < 0 || max_shared_len > max_seq_len) return PKV_EINVAL;
+  const SharedGroups groups = {cu_groups, shared_lens, num_groups, max_group_size,
+                               max_shared_len};
+  return decode_impl(q, k_new, v_new, out_loc, k_cache, v_cache, page_size, num_pages,
+                     page_table, page_table_stride, seq_lens, num_seqs, 1, max_seq_len,
+                     num_q_heads, num_kv_heads, head_dim, softmax_scale, split_tokens, out,
+                     workspace, workspace_bytes, stream, false, &groups);
+}
