@@ -146,6 +146,38 @@ def test_decode_step_noalloc_scratch_size():
         assert 0 < pkv.pkv_decode_workspace_bytes(B, hq, hkv, d, maxlen) <= cap
 
 
+def _shared(**kw):
+    a = dict(q=FAKE, kn=None, vn=None, loc=None, kc=FAKE, vc=FAKE, ps=16, pages=100, pt=FAKE,
+             stride=128, seq=FAKE, B=4, maxlen=2048, cu=FAKE, sh=FAKE, G=2, maxg=3, maxsh=1024,
+             hq=32, hkv=8, d=64, scale=0.125, split=0, out=FAKE, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_paged_attn_decode_shared(
+        a["q"], a["kn"], a["vn"], a["loc"], a["kc"], a["vc"], a["ps"], a["pages"], a["pt"],
+        a["stride"], a["seq"], a["B"], a["maxlen"], a["cu"], a["sh"], a["G"], a["maxg"],
+        a["maxsh"], a["hq"], a["hkv"], a["d"], a["scale"], a["split"], a["out"], a["ws"],
+        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), 1), (dict(sh=None), 1), (dict(G=0), 1), (dict(G=5), 1), (dict(G=-1), 1),
+    (dict(maxg=5), 1), (dict(maxg=-1), 1), (dict(maxsh=4096), 1), (dict(maxsh=-16), 1),
+    (dict(q=None), 1), (dict(hq=30), 1), (dict(kn=FAKE), 1),   # part of the store missing
+    (dict(d=96), 2), (dict(hq=128), 2), (dict(wsb=100), 3),
+    (dict(B=0, G=0, maxg=0, cu=None, sh=None), 0),
+])
+def test_decode_shared_validation(kw, status):
+    assert _shared(**kw) == status
+
+
+def test_decode_shared_workspace_size():
+    plain = pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 2048)
+    shared = pkv.pkv_paged_attn_decode_shared_workspace_bytes(64, 32, 8, 64, 2048, 1024)
+    assert shared > plain   # 16 more partial slots per (request, KV head) for the prefix splits
+    assert pkv.pkv_paged_attn_decode_shared_workspace_bytes(64, 32, 8, 64, 2048, 0) == plain
+    assert pkv.pkv_paged_attn_decode_shared_workspace_bytes(64, 32, 8, 64, 2048, 4096) == 0
+
+
 def test_decode_graphs_validation():
     lib = pkv.lib()
     arr = (ctypes.c_int32 * 3)(1, 2, 4)
