@@ -493,45 +493,77 @@ def time_metadata(steps: int):
     return res
 
 
-def stream_reference(steps: int):
-    """torch's reduction (read only) and copy kernels over `nbytes` buffers,
-    rotating over replicas so the working set (>= 1 GiB) exceeds the 256 MB
-    Infinity Cache; mean per-call time by HIP events after a 0.25 s warm-up.
-    A reference for the decode kernels' bandwidth, not part of the hot path."""
-    import torch
-
+def decode_step_bytes(name: str) -> int:
+    """decode_bytes + store_bytes of a named decode workload, from its
+    lengths alone (no pool is built)."""
     from paged_kv_attention_out_amd import inputs
 
+    cfg = inputs.WORKLOADS[name]
+    n = inputs.draw_lengths(name).astype(np.int64)
+    B, ps = cfg["num_seqs"], cfg["page_size"]
+    hkv, hq, d, ql = cfg["num_kv_heads"], cfg["num_q_heads"], cfg["head_dim"], cfg.get("q_len", 1)
+    kv = int(n.sum()) * hkv * d * 2 * 2
+    qo = 2 * B * ql * hq * d * 2
+    meta = int(((n + ps - 1) // ps).sum()) * 4 + 4 * B
+    store = 2 * B * hkv * d * 2 * 2 + 4 * B if cfg["store_new"] else 0
+    return kv + qo + meta + store
+
+
+STREAM_BLOCKS = (1024, 2048, 4096, 8192)
+
+
+def stream_reference(steps: int):
+    """The device's plain streaming-read rate over each decode workload's
+    step bytes: the library's reference read (`pkv_ref_stream_read`, one
+    contiguous pass, 16-byte loads, eight in flight per thread) at several
+    grid sizes, rotating over replicas so the working set (>= 1 GiB) exceeds
+    the 256 MB Infinity Cache; mean per-call time by HIP events after a
+    0.25 s warm-up.  torch's reduction and copy over the Llama-shaped step
+    bytes are listed beside it.  A reference for the decode kernels'
+    bandwidth, not part of the hot path."""
+    import torch
+
+    import paged_kv_attention_out_amd as pkv
+
+    def timed(call):
+        warm_up(call, 5)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            call(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
     res = {}
-    w = inputs.make_workload(PRIMARY, device="cpu", poison=False)
-    step_bytes = decode_bytes(w) + store_bytes(w)
-    del w
-    for label, nbytes in (("llama_decode_step_bytes", step_bytes), ("1GiB", 1 << 30)):
-        n = (nbytes // 16) * 4           # float32 elements, a multiple of 4
-        R = max(1, math.ceil(MIN_WORKING_SET / (n * 4)))
-        bufs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(R)]
-        dst = torch.empty_like(bufs[0])
-        out = {}
-        for kind in ("sum", "copy"):
-            def call(i):
-                if kind == "sum":
-                    bufs[i % R].sum()
-                else:
-                    dst.copy_(bufs[i % R])
-            warm_up(call, 5)
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(steps)]
-            for i in range(steps):
-                ev[i][0].record()
-                call(i)
-                ev[i][1].record()
-            torch.cuda.synchronize()
-            us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
-            moved = n * 4 * (1 if kind == "sum" else 2)
-            out[kind] = {"us_mean": round(us, 2), "bytes": moved,
-                         "GB/s": round(moved / (us * 1e-6) / 1e9, 1)}
-        res[label] = dict(out, replicas=R)
-        del bufs, dst
+    for name in ("llama_decode", "qwen_decode", "long_decode"):
+        nbytes = decode_step_bytes(name) // 16 * 16
+        R = max(1, math.ceil(MIN_WORKING_SET / nbytes))
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        sink = torch.empty(int(pkv.lib().pkv_ref_stream_sink_words(max(STREAM_BLOCKS))),
+                           dtype=torch.int32, device="cuda")
+        out = {"bytes": nbytes, "replicas": R, "by_blocks": {}}
+        for blocks in STREAM_BLOCKS:
+            us = timed(lambda i: pkv.pkv_ref_stream_read(bufs[i % R], blocks, sink))
+            out["by_blocks"][blocks] = {"us_mean": round(us, 2),
+                                        "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        best = min(out["by_blocks"], key=lambda k: out["by_blocks"][k]["us_mean"])
+        out["best"] = dict(out["by_blocks"][best], blocks=best)
+        if name == PRIMARY:
+            n = nbytes // 4
+            f = [b.view(torch.float32)[:n] for b in bufs]
+            dst = torch.empty_like(f[0])
+            for kind in ("sum", "copy"):
+                call = (lambda i: f[i % R].sum()) if kind == "sum" else \
+                    (lambda i: dst.copy_(f[i % R]))
+                us = timed(call)
+                moved = n * 4 * (1 if kind == "sum" else 2)
+                out["torch_" + kind] = {"us_mean": round(us, 2), "bytes": moved,
+                                        "GB/s": round(moved / (us * 1e-6) / 1e9, 1)}
+            del f, dst
+        res[name] = out
+        del bufs, sink
         torch.cuda.empty_cache()
     return res
 

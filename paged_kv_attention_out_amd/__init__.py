@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     pkv_paged_attn_prefill,
     pkv_prefill_metadata,
     pkv_prefill_workspace_bytes,
+    pkv_ref_stream_read,
     prefill_workspace,
     pkv_store_kv,
     strerror,

@@ -68,6 +68,9 @@ SIGNATURES = {
     "pkv_paged_attn_decode_multi": (ctypes.c_int, [
         _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _i32, _c_void_p, _i32,
         _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p, _c_void_p, _size, _c_void_p]),
+    # include/pkv_ref.h: the streaming-read reference (measurement only)
+    "pkv_ref_stream_sink_words": (_size, [_i32]),
+    "pkv_ref_stream_read": (ctypes.c_int, [_c_void_p, _size, _i32, _c_void_p, _c_void_p]),
 }
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -529,6 +532,24 @@ def pkv_decode_metadata(seq_lens: torch.Tensor, page_table: torch.Tensor, page_s
                                      page_size, _ptr(out_loc), _stream(seq_lens)),
            "pkv_decode_metadata")
     return out_loc
+
+
+def pkv_ref_stream_read(src: torch.Tensor, blocks: int,
+                        sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One plain streaming read of ``src`` (contiguous device memory, a
+    multiple of 16 bytes) by ``blocks`` workgroups; returns the sink (one
+    word per wavefront).  A bandwidth reference, not part of the path."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    words = int(lib().pkv_ref_stream_sink_words(blocks))
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=src.device)
+    _numel(sink, words, "sink", at_least=True)
+    _dev(sink, torch.int32, "sink")
+    _check(lib().pkv_ref_stream_read(_ptr(src), nbytes, blocks, _ptr(sink), _stream(src)),
+           "pkv_ref_stream_read")
+    return sink
 
 
 def pkv_prefill_workspace_bytes() -> int:

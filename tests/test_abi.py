@@ -1,10 +1,11 @@
-"""The C ABI on the host: the library loads, exports what include/pkv.h
+"""The C ABI on the host: the library loads, exports what include/*.h
 declares, and rejects bad arguments before anything is enqueued.
 
 Every call here fails host-side validation, so no kernel is ever launched
 (the fake device pointers below are never dereferenced)."""
 
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -15,14 +16,16 @@ import paged_kv_attention_out_amd as pkv
 from paged_kv_attention_out_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pkv.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 FAKE = 1 << 20  # 16-byte aligned, never dereferenced: every call below fails validation
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -310,3 +313,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+@pytest.mark.parametrize("src,nbytes,blocks,sink,status", [
+    (FAKE, 1 << 20, 0, FAKE, 1), (FAKE, 1 << 20, (1 << 20) + 1, FAKE, 1),
+    (None, 1 << 20, 64, FAKE, 1), (FAKE, 1 << 20, 64, None, 1),
+    (FAKE + 8, 1 << 20, 64, FAKE, 1), (FAKE, (1 << 20) + 8, 64, FAKE, 1),
+    (None, 0, 64, None, 0),
+])
+def test_ref_stream_read_validation(src, nbytes, blocks, sink, status):
+    assert pkv.lib().pkv_ref_stream_read(src, nbytes, blocks, sink, None) == status
+
+
+def test_ref_stream_sink_words():
+    lib = pkv.lib()
+    assert lib.pkv_ref_stream_sink_words(0) == 0
+    assert lib.pkv_ref_stream_sink_words(-3) == 0
+    assert lib.pkv_ref_stream_sink_words(10) == 40
