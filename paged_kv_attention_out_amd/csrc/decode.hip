@@ -713,13 +713,13 @@ __global__ __launch_bounds__(256, 2) void prefix_pass_kernel(pkv_prefix::Params 
 }
 
 // The loads of a batch of splits do not depend on the request length: the
-// partials of every split up to the host bound are read at once (in bounds
-// of the workspace; stale entries past the request's last split are never
-// used), so the kernel costs one memory round trip for the length and one
-// for the partials, not a chain of them.
-constexpr int kCombineBatch = 16;  // splits whose o rows are in flight together
-
-template <int D, int G>
+// partials of a batch of KB splits are read at once (in bounds of the
+// workspace; stale entries past the request's last split are never used),
+// so a request of up to KB splits costs one memory round trip, not a chain
+// of them.  KB is 16, or 64 when the host bound allows more than 16 splits
+// (long requests): fewer, larger batches keep more bytes in flight for the
+// few waves such batches have.
+template <int D, int G, int KB>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   constexpr int DPL = D / 64;  // output dims per lane
   const int QL = p.q_len;
@@ -746,12 +746,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   // device-chosen split the units fit one round, so requests have few
   // splits: only 8 are fetched ahead (the bound nsm, from the host split,
   // can be far above the real count), the rest once the count is known.
-  const int pre = min(nsm, p.round_units > 0 ? 8 : kCombineBatch);
+  const int pre = min(nsm, p.round_units > 0 ? 8 : KB);
   float mv = lane < nsm ? om[(int64_t)lane * NC] : kNegInf;
   float lv = lane < nsm ? ol[(int64_t)lane * NC] : 0.f;
-  float v[kCombineBatch][DPL];
+  float v[KB][DPL];
 #pragma unroll
-  for (int k = 0; k < kCombineBatch; ++k)
+  for (int k = 0; k < KB; ++k)
 #pragma unroll
     for (int i = 0; i < DPL; ++i) v[k][i] = k < pre ? oo[(int64_t)k * NC * D + 64 * i] : 0.f;
 
@@ -787,18 +787,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     L += t;
     // lane = output dim; the weights of the 64 splits are broadcast by readlane
     const int cnt = min(64, ns - s0);
-    for (int k0 = 0; k0 < cnt; k0 += kCombineBatch) {
+    for (int k0 = 0; k0 < cnt; k0 += KB) {
       // later batches load now; the first came with the length, unless it
       // holds more splits than were fetched ahead (then it is read again)
-      if (s0 + k0 != 0 || min(cnt, kCombineBatch) > pre) {
+      if (s0 + k0 != 0 || min(cnt, KB) > pre) {
 #pragma unroll
-        for (int k = 0; k < kCombineBatch; ++k)
+        for (int k = 0; k < KB; ++k)
 #pragma unroll
           for (int i = 0; i < DPL; ++i)
             v[k][i] = k0 + k < cnt ? oo[(int64_t)(s0 + k0 + k) * NC * D + 64 * i] : 0.f;
       }
 #pragma unroll
-      for (int k = 0; k < kCombineBatch; ++k) {
+      for (int k = 0; k < KB; ++k) {
         if (k0 + k < cnt) {
           const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + k));
 #pragma unroll
@@ -985,7 +985,10 @@ int launch_decode(DecodeParams p, int64_t waves, hipStream_t s,
   }
   if (st != PKV_OK || p.n_split_max <= 1) return st;
   const int64_t cblocks = ((int64_t)p.num_seqs * p.q_len * p.num_q_heads + 3) / 4;
-  return pkv_host::launch(decode_combine_kernel<D, G>, dim3((unsigned)cblocks), dim3(256), s,
+  if (p.n_split_max > 16)
+    return pkv_host::launch(decode_combine_kernel<D, G, 64>, dim3((unsigned)cblocks), dim3(256),
+                            s, p);
+  return pkv_host::launch(decode_combine_kernel<D, G, 16>, dim3((unsigned)cblocks), dim3(256), s,
                           p);
 }
 
