@@ -187,7 +187,7 @@ __device__ int device_split(const DecodeParams& p, const Lens4& lens) {
   const int* len = lens.v;  // -1: no request
   const int nk = (p.num_seqs + 63) >> 6;  // chunks of 64 requests that exist
   auto units = [&](int x) {  // max(ceil(n / x), 1) per request, summed (exact)
-    const float inv = 1.f / (float)x;
+    const float inv = __builtin_amdgcn_rcpf((float)x);  // the integer corrections below absorb its error
     int u = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
