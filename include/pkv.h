@@ -90,7 +90,9 @@ int pkv_store_kv(const void* k_new, const void* v_new, const int32_t* out_loc,
 /*
  * pkv_decode_workspace_bytes -- size of the workspace pkv_paged_attn_decode
  * needs for these arguments (0 when every request fits one split).  Pass the
- * same split_tokens (0 = automatic) as to the decode call.
+ * same split_tokens (0 = automatic) as to the decode call.  Invalid shapes,
+ * and shapes whose split partials would exceed 2^46 bytes, also give 0; the
+ * decode call rejects the latter with PKV_EINVAL.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,
@@ -304,7 +306,8 @@ size_t pkv_paged_attn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t nu
  * The graphs belong to the device current at creation.
  *
  *   buckets      : num_buckets (1 .. 64) distinct positive batch sizes, any
- *                  order
+ *                  order (pkv_decode_graphs_workspace_bytes returns 0 for
+ *                  any other list)
  *   graphs       : receives the handle (NULL on error)
  *   all others   : as pkv_decode_step, for the largest bucket
  *

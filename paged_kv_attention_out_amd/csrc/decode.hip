@@ -824,11 +824,11 @@ constexpr int kMinAutoSplit = 128;
 int32_t choose_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                      int32_t split_tokens) {
   if (split_tokens != 0) return split_tokens;
-  int32_t s = (max_seq_len + 15) / 16 * 16;
+  int64_t s = ((int64_t)max_seq_len + 15) / 16 * 16;
   const int64_t rk = (int64_t)num_seqs * num_kv_heads;
-  while (s > kMinAutoSplit && rk * ((max_seq_len + s - 1) / s) < kTargetUnits)
+  while (s > kMinAutoSplit && rk * (((int64_t)max_seq_len + s - 1) / s) < kTargetUnits)
     s = (s / 2 + 15) / 16 * 16;
-  return s;
+  return (int32_t)std::min<int64_t>(s, (int64_t)1 << 30);
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -837,9 +837,12 @@ struct WsLayout {
   size_t m, l, o, split, total;
 };
 
-// ncols = query columns per (request, KV head): g * q_len
+// ncols = query columns per (request, KV head): g * q_len.  total == 0
+// when the partials would take more than 2^46 bytes (no such call is valid).
 WsLayout ws_layout(int64_t rk, int64_t nsm, int64_t ncols, int d) {
-  WsLayout w;
+  WsLayout w = {};
+  const __int128 o_bytes = (__int128)rk * nsm * ncols * d * (int64_t)sizeof(float);
+  if (rk < 0 || nsm < 0 || ncols < 0 || d < 0 || o_bytes > ((__int128)1 << 46)) return w;
   w.m = 0;
   w.l = w.m + align256(rk * nsm * ncols * sizeof(float));
   w.o = w.l + align256(rk * nsm * ncols * sizeof(float));
@@ -1028,7 +1031,7 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
                        split_tokens))
     return 0;
   const int32_t s = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
-  const int64_t nsm = (max_seq_len + s - 1) / s;
+  const int64_t nsm = ((int64_t)max_seq_len + s - 1) / s;
   if (nsm <= 1 || num_seqs == 0) return 0;
   return ws_layout((int64_t)num_seqs * num_kv_heads, nsm, num_q_heads / num_kv_heads, head_dim)
       .total;
@@ -1043,7 +1046,7 @@ extern "C" size_t pkv_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_l
     return 0;
   if (q_len < 1 || q_len > kMaxQueryLen) return 0;
   const int32_t s = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
-  const int64_t nsm = (max_seq_len + s - 1) / s;
+  const int64_t nsm = ((int64_t)max_seq_len + s - 1) / s;
   if (nsm <= 1 || num_seqs == 0) return 0;
   return ws_layout((int64_t)num_seqs * num_kv_heads, nsm,
                    (int64_t)q_len * (num_q_heads / num_kv_heads), head_dim)
@@ -1145,7 +1148,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   if (g != 1 && g != 2 && g != 4 && g != 8) return PKV_EUNSUPPORTED;
 
   const int32_t split = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
-  const int64_t nsm = (max_seq_len + split - 1) / split;
+  const int64_t nsm = ((int64_t)max_seq_len + split - 1) / split;
   // partial slots of the shared-prefix pass, ahead of the splits
   const int64_t nks = groups == nullptr ? 0
                                         : ((int64_t)(groups->max_shared_len & ~15) +
@@ -1157,6 +1160,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   DecodeParams p = {};
   if (slots > 1) {
     const WsLayout w = ws_layout(rk, slots, (int64_t)g * q_len, head_dim);
+    if (w.total == 0) return PKV_EINVAL;  // partials beyond any device memory
     if (use_scratch) {  // the library's fixed scratch instead of a caller workspace
       workspace_bytes = kScratchBytes;
       if (workspace_bytes < w.total) return PKV_ENOSPACE;
@@ -1395,9 +1399,13 @@ extern "C" size_t pkv_decode_graphs_workspace_bytes(const int32_t* buckets, int3
                                                     int32_t head_dim, int32_t max_seq_len) {
   if (buckets == nullptr || num_buckets <= 0 || num_buckets > kMaxGraphBuckets) return 0;
   size_t need = 0;
-  for (int i = 0; i < num_buckets; ++i)
+  for (int i = 0; i < num_buckets; ++i) {
+    if (buckets[i] <= 0) return 0;  // as pkv_decode_graphs_create rejects it
+    for (int j = 0; j < i; ++j)
+      if (buckets[j] == buckets[i]) return 0;
     need = std::max(need, pkv_decode_workspace_bytes(buckets[i], num_q_heads, num_kv_heads,
                                                      head_dim, max_seq_len, 0));
+  }
   return need;
 }
 
@@ -1515,7 +1523,7 @@ extern "C" size_t pkv_paged_attn_decode_shared_workspace_bytes(
   const int32_t s = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
   const int64_t slots = ((int64_t)(max_shared_len & ~15) + pkv_prefix::kSplit - 1) /
                             pkv_prefix::kSplit +
-                        (max_seq_len + s - 1) / s;
+                        ((int64_t)max_seq_len + s - 1) / s;
   if (slots <= 1) return 0;
   return ws_layout((int64_t)num_seqs * num_kv_heads, slots, num_q_heads / num_kv_heads, head_dim)
       .total;

@@ -611,7 +611,7 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   if (!(g == 1 || g == 2 || g == 4 || g == 8)) return PKV_EUNSUPPORTED;
   if (workspace_bytes < kPrefillWorkspaceBytes) return PKV_ENOSPACE;
   const int qtile = 128 * nb / g;
-  const int64_t n_qtiles = (max_q_len + qtile - 1) / qtile;
+  const int64_t n_qtiles = ((int64_t)max_q_len + qtile - 1) / qtile;
   const int64_t n_items = n_qtiles * num_seqs * num_kv_heads;
   if (n_items >= INT32_MAX / 2) return PKV_EINVAL;
   // Row addresses are formed from a 32-bit page size and a 24-bit in-page

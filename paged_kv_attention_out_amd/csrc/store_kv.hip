@@ -50,7 +50,7 @@ extern "C" int pkv_store_kv(const void* k_new, const void* v_new, const int32_t*
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_EINVAL;
   const int64_t pieces_per_row = (int64_t)num_kv_heads * head_dim / 8;
-  if (pieces_per_row > INT32_MAX) return PKV_EINVAL;
+  if (pieces_per_row > INT32_MAX || num_tokens > INT64_MAX / pieces_per_row) return PKV_EINVAL;
   const int64_t num_pieces = num_tokens * pieces_per_row;
   const int64_t blocks = (num_pieces + 255) / 256;
   if (blocks > INT32_MAX) return PKV_EINVAL;
