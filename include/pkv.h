@@ -125,7 +125,12 @@ int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
  * over j = 0 .. seq_lens[r]-1, with K[r, j, kvh] the row of slot
  * page_table[r, j / page_size] * page_size + j % page_size.  Long contexts
  * are cut into splits of split_tokens tokens that run in parallel; a second
- * kernel on the same stream merges the splits (flash-decoding).
+ * kernel on the same stream merges the splits (flash-decoding).  With the
+ * automatic split, a batch of at most 256 requests and 8 KV heads that
+ * needs several rounds of units is instead shared evenly by one round of
+ * workgroups (pieces cut at 16-token boundaries), when the workspace holds
+ * the pieces' partials (pkv_decode_workspace_bytes counts them); the
+ * result is the same up to rounding.
  *
  *   q            : [num_seqs, num_q_heads, head_dim] bf16
  *   k_cache,

@@ -70,6 +70,14 @@ struct DecodeParams {
   float* ws_l;
   float* ws_o;  // [B * Hkv * n_split_max * g * D]
   int32_t* ws_split;  // the split the split kernel used (read by the combine)
+  // Balanced launch (decode_balanced_kernel): partial rows of its pieces and
+  // per (request, KV head) the first row and the row count; null when the
+  // workspace does not hold them.
+  float* bal_m;
+  float* bal_l;
+  float* bal_o;
+  int32_t* bal_table;
+  int32_t auto_split;  // the split is the automatic one (a caller's split is kept)
   int64_t num_pages;
   int32_t page_size;
   int32_t page_shift;
@@ -247,6 +255,12 @@ struct DecodeTraits {
 
 // Per-split kernel, one wavefront per (request, KV head, split).
 //
+// One piece of a balanced launch (decode_balanced_kernel): tokens
+// [t0, t1) of request r's KV head kvh (n tokens in all), partial row `id`.
+struct Piece {
+  int r, kvh, n, t0, t1, id;
+};
+
 // Per group of 16 tokens (lane l: token l%16 of the group, c = l/16):
 //   S^T = K Q^T on MFMA 16x16x32: A = the K rows as loaded (lane l holds 8
 //   dims 32kk+8c.. of token l%16), B = Q^T (column n = query head n % G,
@@ -265,9 +279,12 @@ struct DecodeTraits {
 //   row 4c+i is query head i % G.
 // SKIP: requests may skip their shared-prefix tokens (p.skip); compiled
 // out of the kernels of plain decode.
-template <int D, int G, int LQ, bool SKIP>
+// BAL: the unit is the given piece of a balanced launch (LQ == 1, no
+// skipped tokens) instead of the one `bid` selects.
+template <int D, int G, int LQ, bool SKIP, bool BAL = false>
 __device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const uint32_t bid,
-                                                  uint16_t* vlds_block) {
+                                                  uint16_t* vlds_block,
+                                                  const Piece* piece = nullptr) {
   constexpr int KCH = D / 32;  // 16-byte pieces per lane per row == QK MFMAs per group
   constexpr int NT = D / 16;   // 16-dim tiles of the output == PV MFMAs per pair
   constexpr int NBUF = DecodeTraits<D, G>::NBUF;
@@ -295,12 +312,13 @@ __device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const u
   // columns) the slices of one unit are Hkv / heads_per_block blocks apart:
   // with that a multiple of 8 they share an XCD, so the second slice reads
   // K/V from L2.
+  static_assert(!BAL || (LQ == 1 && !SKIP), "balanced pieces are single-token decode");
   const uint32_t hblocks = (uint32_t)(p.num_kv_heads / p.heads_per_block);  // blocks per unit
   const uint32_t u = bid / hblocks;
   const uint32_t rank = LQ == 1 ? u : u / (uint32_t)p.q_slices;
   const int tq0 = LQ == 1 ? 0 : (int)(u % (uint32_t)p.q_slices) * LQ;  // first query token
   const int QL = LQ == 1 ? 1 : p.q_len;
-  const int kvh = (int)((bid + rank) % hblocks) * p.heads_per_block + wv;
+  const int kvh = BAL ? piece->kvh : (int)((bid + rank) % hblocks) * p.heads_per_block + wv;
   // The first 256 request lengths: four loads at clamped indices, issued
   // together (one memory round trip; the empty asm keeps the compiler from
   // moving each load into a branch of its own).  Then, not waited for with
@@ -312,8 +330,8 @@ __device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const u
   // here (-1, as a missing request).
   Lens4 lens;
   int skv[4] = {0, 0, 0, 0};
-  int pf;
-  {
+  int pf = 0;
+  if constexpr (!BAL) {
     int x[4], y[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[k] = p.seq_lens[min(64 * k + lane, p.num_seqs - 1)];
@@ -333,10 +351,13 @@ __device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const u
       lens.v[k] = 64 * k + lane < p.num_seqs && (skv[k] == 0 || w > 0) ? w : -1;
     }
   }
-  const int sl = device_split(p, lens);  // tokens per split
-  if (p.ws_split != nullptr && bid == 0 && threadIdx.x == 0) *p.ws_split = sl;
+  const int sl = BAL ? 0 : device_split(p, lens);  // tokens per split
+  if (!BAL && p.ws_split != nullptr && bid == 0 && threadIdx.x == 0) *p.ws_split = sl;
   int r = -1, split = 0, n = 0, skip = 0;  // n: work tokens after the skipped ones
-  {
+  if constexpr (BAL) {
+    r = piece->r;
+    n = piece->n;
+  } else {
     // Units in two parts: first every full-length split of every request
     // (request-major), then the short last split of each request whose
     // length is not a multiple of the split (and the one unit of an empty
@@ -391,7 +412,7 @@ __device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const u
   // Query token of the column; columns past the last token repeat it and
   // are never written.
   const int tq = min(tq0 + col / G, QL - 1);
-  const int t_begin = skip + split * sl;
+  const int t_begin = BAL ? piece->t0 : skip + split * sl;
 
   // Q^T fragments (B operand): column j holds query token tq of head
   // kvh*G + hcol (the NC columns repeat over the 16 MFMA columns).
@@ -416,7 +437,7 @@ __device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const u
     ptv = (v < 0 || (int64_t)v >= p.num_pages) ? 0 : v;  // keep accesses in the pool
   };
   load_window(t_begin >> p.page_shift);
-  asm volatile("" ::"v"(pf));  // keeps the prefetch; its wait comes with the window's
+  if (!BAL) asm volatile("" ::"v"(pf));  // keeps the prefetch; its wait comes with the window's
 
   if (n <= 0) {
     if (split == 0) {
@@ -430,17 +451,18 @@ __device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const u
     }
     return;
   }
-  const int ns = (n + sl - 1) / sl;
-  const int t_end = min(skip + n, t_begin + sl);
+  const int ns = BAL ? 0 : (n + sl - 1) / sl;
+  const int t_end = BAL ? piece->t1 : min(skip + n, t_begin + sl);
   // The output is written directly only when this split is the request's
   // one partial; otherwise partials go to the workspace.
-  const bool direct = ns == 1 && slot0 == 0;
+  const bool direct = BAL ? piece->t0 == 0 && piece->t1 == n : ns == 1 && slot0 == 0;
+  const bool last = BAL ? t_end == n : split == ns - 1;  // holds the newest token
 
   const int64_t row_elems = (int64_t)p.num_kv_heads * D;
   // Fused step: the request's last split writes this head's slice of the
   // new token's K/V rows to slot out_loc[r] (out-of-range slots are
   // skipped).  No wave of this call reads that slot from the pool.
-  if (LQ == 1 && p.k_new != nullptr && split == ns - 1 && lane < D / 8) {
+  if (LQ == 1 && p.k_new != nullptr && last && lane < D / 8) {
     const int64_t slot = p.out_loc[r];
     if (slot >= 0 && slot < p.num_slots) {
       const int64_t src = ((int64_t)r * p.num_kv_heads + kvh) * D + 8 * lane;
@@ -670,7 +692,8 @@ __device__ __forceinline__ void decode_split_unit(const DecodeParams& p, const u
     } else {
       // Partial (m, l, un-normalised o) of this split for column (tx, h)
       // among the QL * G columns of the request's KV head.
-      const int64_t base = (rk * p.n_split_max + slot0 + split) * (QL * G) + tx * G + h;
+      const int64_t base =
+          (BAL ? (int64_t)piece->id : rk * p.n_split_max + slot0 + split) * (QL * G) + tx * G + h;
       float* dst = p.ws_o + base * D + dl;
 #pragma unroll
       for (int t = 0; t < NT; ++t) dst[16 * t] = o[t][i];
@@ -686,6 +709,157 @@ template <int D, int G, int LQ, bool SKIP = false>
 __global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_split_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t vlds_block[];
   decode_split_unit<D, G, LQ, SKIP>(p, blockIdx.x, vlds_block);
+}
+
+// Balanced decode of a batch that needs several rounds of units.  With one
+// block per (request, split) the dispatcher starts units as slots free up,
+// and the launch ends with a last round of long units draining one by one
+// (on the Qwen-shaped batch the slots are busy 85% of the time).  Here one
+// round of workgroups shares the work exactly: the batch is one sequence of
+// 16-token blocks -- request by request, block by block (a request's last
+// block may be partial) -- of total H, and workgroup g of W takes blocks
+// [g Q, (g + 1) Q), Q = ceil(H / W), with one wave per KV head, so a
+// workgroup reads whole token rows as a plain streaming read would.  Its
+// range covers the end of one request, whole requests and the start of
+// another; each such piece starts on a 16-token boundary (as every unit
+// does: a group of 16 tokens never crosses a page) and is attended as a
+// unit by every wave for its head, leaving a partial, or the output itself
+// when the piece is the whole request.  A piece starting at block a of
+// request r has partial row r + floor(a / Q) (per KV head): rows rise
+// through the batch, a request's rows are consecutive, and its first piece
+// records the first row and the row count for the merge.  At most 256
+// requests (their lengths stay in registers) and 8 KV heads.
+constexpr int kBalMaxSeqs = 256;
+constexpr int kBalMaxWaves = 4096;  // waves at most (partial rows kept for the cut points)
+
+template <int D, int G>
+__global__ __launch_bounds__(512, 2) PKV_DECODE_OCC void decode_balanced_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t vlds_block[];
+  const int lane = threadIdx.x & 63;
+  const int kvh = (int)(threadIdx.x >> 6);  // one wave per KV head
+  const uint32_t W = gridDim.x;
+  const int hkv = p.num_kv_heads;
+  // Lengths (lane = request within a chunk of 64) and their 16-token blocks,
+  // scanned per chunk; base[k]: blocks before chunk k.
+  int len[4], inc[4];
+  uint32_t base[5];
+  {
+    int x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = p.seq_lens[min(64 * k + lane, p.num_seqs - 1)];
+    base[0] = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      len[k] = 64 * k + lane < p.num_seqs ? min(max(x[k], 0), p.max_seq_len) : 0;
+      inc[k] = wave_incl_scan((len[k] + 15) >> 4);
+      base[k + 1] = base[k] + (uint32_t)__builtin_amdgcn_readlane(inc[k], 63);
+    }
+  }
+  const uint32_t H = base[4];
+  if (H == 0) return;  // no keys at all: the merge writes the zero rows
+  const uint32_t Q = (H + W - 1) / W;
+  uint32_t a = blockIdx.x * Q;
+  const uint32_t e = min(a + Q, H);
+  while (a < e) {
+    // the request holding block a: its chunk, then its lane
+    const int k = a < base[1] ? 0 : a < base[2] ? 1 : a < base[3] ? 2 : 3;
+    const int lk = k == 0 ? len[0] : k == 1 ? len[1] : k == 2 ? len[2] : len[3];
+    const int ik = k == 0 ? inc[0] : k == 1 ? inc[1] : k == 2 ? inc[2] : inc[3];
+    const uint32_t bk = k == 0 ? base[0] : k == 1 ? base[1] : k == 2 ? base[2] : base[3];
+    const uint64_t hit = __ballot((uint32_t)ik > a - bk);
+    const int lr = (int)__builtin_ctzll(hit);
+    const int n = __builtin_amdgcn_readlane(lk, lr);  // > 0: block a lies in it
+    const uint32_t nb = (uint32_t)((n + 15) >> 4);
+    const uint32_t rbase = bk + (uint32_t)__builtin_amdgcn_readlane(ik, lr) - nb;
+    const uint32_t send = min(e, rbase + nb);
+    const int r = 64 * k + lr;
+    const int row = (int)((uint32_t)r + a / Q);
+    Piece pc;
+    pc.r = r;
+    pc.kvh = kvh;
+    pc.n = n;
+    pc.t0 = (int)(a - rbase) * 16;
+    pc.t1 = min((int)(send - rbase) * 16, n);
+    pc.id = row * hkv + kvh;
+    if (pc.t0 == 0 && threadIdx.x == 0) {
+      p.bal_table[2 * r] = row;
+      p.bal_table[2 * r + 1] = (int)((rbase + nb - 1) / Q - rbase / Q + 1);
+    }
+    decode_split_unit<D, G, 1, false, true>(p, 0, vlds_block, &pc);
+    a = send;
+  }
+}
+
+// The merge of a balanced launch: one wave per (request, query head).  A
+// request without keys gets a zero row; a sequence that was one piece was
+// written by it; otherwise its rows (first, count) are merged as in
+// decode_combine_kernel.
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_combine_balanced_kernel(DecodeParams p) {
+  constexpr int DPL = D / 64;
+  constexpr int KB = 16;  // rows whose o is in flight together
+  const int lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rh >= (int64_t)p.num_seqs * p.num_q_heads) return;
+  const int r = (int)(rh / p.num_q_heads);
+  const int qh = (int)(rh % p.num_q_heads);
+  const int kvh = qh / G, hc = qh % G;
+  const int32_t* t = p.bal_table + 2 * (int64_t)r;
+  int n = p.seq_lens[r];
+  int first = t[0], count = t[1];
+  n = uniform(n);
+  uint16_t* out = p.out + ((int64_t)r * p.num_q_heads + qh) * D;
+  if (min(n, p.max_seq_len) <= 0) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) out[lane + 64 * i] = 0;
+    return;
+  }
+  const int ns = uniform(count);
+  if (ns <= 1) return;  // written by its one piece
+  // rows first .. first + count - 1, this KV head's partials of each
+  const int64_t row0 = (int64_t)uniform(first) * p.num_kv_heads + kvh;
+  const int64_t stride = (int64_t)p.num_kv_heads * G;  // floats between rows (m, l)
+  const float* om = p.bal_m + row0 * G + hc;
+  const float* ol = p.bal_l + row0 * G + hc;
+  const float* oo = p.bal_o + (row0 * G + hc) * D + lane;
+  float M = kNegInf;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    float y = s0 + lane < ns ? om[(int64_t)(s0 + lane) * stride] : kNegInf;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) y = fmaxf(y, __shfl_xor(y, off));
+    M = fmaxf(M, y);
+  }
+  float L = 0.f, acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int sidx = s0 + lane;
+    const float w = sidx < ns ? fast_exp2(om[(int64_t)sidx * stride] - M) : 0.f;
+    float tl = sidx < ns ? ol[(int64_t)sidx * stride] * w : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tl += __shfl_xor(tl, off);
+    L += tl;
+    const int cnt = min(64, ns - s0);
+    for (int k0 = 0; k0 < cnt; k0 += KB) {
+      float v[KB][DPL];
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+#pragma unroll
+        for (int i = 0; i < DPL; ++i)
+          v[k][i] = k0 + k < cnt ? oo[(int64_t)(s0 + k0 + k) * stride * D + 64 * i] : 0.f;
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        if (k0 + k < cnt) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k0 + k));
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) acc[i] = fmaf(v[k][i], wk, acc[i]);
+        }
+      }
+    }
+  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) out[lane + 64 * i] = to_bf16(acc[i] * inv);
 }
 
 // The split kernel for batches with shared prefixes: the grid's first
@@ -833,6 +1007,32 @@ int32_t choose_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
+// Layout of the balanced launch's partial rows (decode_balanced_kernel) in
+// the same workspace as the split layout (a call uses one of the two),
+// after the first 256 bytes: B + kBalMaxWaves / Hkv rows of Hkv x g
+// columns, then the (first row, count) table per request.  Only for batches of at
+// most kBalMaxSeqs requests and 8 KV heads whose tokens count well below
+// 2^31.
+struct BalLayout {
+  size_t m, l, o, table, total;
+};
+bool bal_eligible(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads, int64_t head_dim,
+                  int64_t max_seq_len) {
+  return num_seqs >= 1 && num_seqs <= kBalMaxSeqs && num_kv_heads <= 8 &&
+         num_q_heads <= 8 * num_kv_heads && head_dim <= 128 &&
+         num_seqs * max_seq_len + 16 * (int64_t)kBalMaxWaves < ((int64_t)1 << 31);
+}
+BalLayout bal_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t g, int64_t d) {
+  const int64_t rows = num_seqs * num_kv_heads + kBalMaxWaves;
+  BalLayout b;
+  b.m = 256;
+  b.l = b.m + align256(rows * g * sizeof(float));
+  b.o = b.l + align256(rows * g * sizeof(float));
+  b.table = b.o + align256(rows * g * d * sizeof(float));
+  b.total = b.table + align256(num_seqs * 2 * sizeof(int32_t));
+  return b;
+}
+
 struct WsLayout {
   size_t m, l, o, split, total;
 };
@@ -843,11 +1043,11 @@ WsLayout ws_layout(int64_t rk, int64_t nsm, int64_t ncols, int d) {
   WsLayout w = {};
   const __int128 o_bytes = (__int128)rk * nsm * ncols * d * (int64_t)sizeof(float);
   if (rk < 0 || nsm < 0 || ncols < 0 || d < 0 || o_bytes > ((__int128)1 << 46)) return w;
-  w.m = 0;
+  w.split = 0;  // first 256 bytes: the split the split kernel used
+  w.m = 256;
   w.l = w.m + align256(rk * nsm * ncols * sizeof(float));
   w.o = w.l + align256(rk * nsm * ncols * sizeof(float));
-  w.split = w.o + align256(rk * nsm * ncols * d * sizeof(float));
-  w.total = w.split + 256;
+  w.total = w.o + align256(rk * nsm * ncols * d * sizeof(float));
   return w;
 }
 
@@ -876,10 +1076,12 @@ bool decode_shape_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
 
 // Waves of decode_split_kernel<D, G, LQ> resident on the current device at
 // once with hpb waves per workgroup (occupancy x CUs, cached per device).
-template <int D, int G, int LQ>
+template <int D, int G, int LQ, bool BALANCED = false>
 int resident_waves(int hpb) {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices][4];  // by log2(hpb)
+  const void* kernel = BALANCED ? reinterpret_cast<const void*>(decode_balanced_kernel<D, G>)
+                                : reinterpret_cast<const void*>(decode_split_kernel<D, G, LQ>);
   constexpr size_t kWaveLds = (size_t)DecodeTraits<D, G>::NBUF * 16 * (D + 8) * sizeof(uint16_t);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
@@ -891,9 +1093,8 @@ int resident_waves(int hpb) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(decode_split_kernel<D, G, LQ>), 64 * hpb,
-          kWaveLds * hpb) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * hpb, kWaveLds * hpb) !=
+      hipSuccess)
     return 0;
   const int n = cus * per_cu * hpb;
   if (n > 0 && dev < kMaxDevices) cache[dev][slot].store(n, std::memory_order_relaxed);
@@ -978,6 +1179,24 @@ int launch_decode(DecodeParams p, int64_t waves, hipStream_t s,
     } else if (p.skip != nullptr) {
       st = pkv_host::launch(decode_split_kernel<D, G, 1, true>, dim3((unsigned)blocks),
                             dim3(64 * p.heads_per_block), s, p, kWaveLds * p.heads_per_block);
+    } else if (p.auto_split && p.round_units == 0 && p.bal_table != nullptr && hkv <= 8 &&
+               !(hkv & (hkv - 1)) &&
+               resident_waves<D, G, 1, true>(hkv) > 0 &&
+               blocks * hpb > resident_waves<D, G, 1, true>(hkv)) {
+      // several rounds of units: one round of workgroups (a wave per KV
+      // head) sharing the work exactly
+      DecodeParams pb = p;
+      pb.ws_m = p.bal_m;
+      pb.ws_l = p.bal_l;
+      pb.ws_o = p.bal_o;
+      pb.heads_per_block = hkv;
+      const int64_t nblk = std::min(resident_waves<D, G, 1, true>(hkv), kBalMaxWaves) / hkv;
+      st = pkv_host::launch(decode_balanced_kernel<D, G>, dim3((unsigned)nblk),
+                            dim3(64 * hkv), s, pb, kWaveLds * hkv);
+      if (st != PKV_OK) return st;
+      const int64_t cb = ((int64_t)p.num_seqs * p.num_q_heads + 3) / 4;
+      return pkv_host::launch(decode_combine_balanced_kernel<D, G>, dim3((unsigned)cb), dim3(256),
+                              s, pb);
     } else {
       st = pkv_host::launch(decode_split_kernel<D, G, LQ>, dim3((unsigned)blocks),
                             dim3(64 * p.heads_per_block), s, p, kWaveLds * p.heads_per_block);
@@ -1033,8 +1252,15 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
   const int32_t s = choose_split(num_seqs, num_kv_heads, max_seq_len, split_tokens);
   const int64_t nsm = ((int64_t)max_seq_len + s - 1) / s;
   if (nsm <= 1 || num_seqs == 0) return 0;
-  return ws_layout((int64_t)num_seqs * num_kv_heads, nsm, num_q_heads / num_kv_heads, head_dim)
-      .total;
+  const size_t split_total =
+      ws_layout((int64_t)num_seqs * num_kv_heads, nsm, num_q_heads / num_kv_heads, head_dim)
+          .total;
+  if (split_total == 0 ||
+      !bal_eligible(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len))
+    return split_total;
+  return std::max(split_total, bal_layout(num_seqs, num_kv_heads, num_q_heads / num_kv_heads,
+                                          head_dim)
+                                   .total);
 }
 
 extern "C" size_t pkv_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len,
@@ -1174,6 +1400,16 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
     p.ws_l = reinterpret_cast<float*>(ws + w.l);
     p.ws_o = reinterpret_cast<float*>(ws + w.o);
     p.ws_split = reinterpret_cast<int32_t*>(ws + w.split);
+    if (q_len == 1 && groups == nullptr &&
+        bal_eligible(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len)) {
+      const BalLayout b = bal_layout(num_seqs, num_kv_heads, g, head_dim);
+      if (workspace_bytes >= b.total) {
+        p.bal_m = reinterpret_cast<float*>(ws + b.m);
+        p.bal_l = reinterpret_cast<float*>(ws + b.l);
+        p.bal_o = reinterpret_cast<float*>(ws + b.o);
+        p.bal_table = reinterpret_cast<int32_t*>(ws + b.table);
+      }
+    }
   }
   // One wave per (request, split) pair, KV head and query slice: at most
   // this many waves, those past the pairs that exist exit at once.
@@ -1206,6 +1442,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
   // Device-chosen split (see device_split): only for the automatic split and
   // batches that need few rounds even at the longest length.
   p.round_units = split_tokens == 0 && num_seqs <= 256 ? -1 : 0;
+  p.auto_split = split_tokens == 0;
   p.q_len = q_len;
   p.q_slices = slices;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;

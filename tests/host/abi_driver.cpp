@@ -55,7 +55,7 @@ int main() {
             for (int32_t ql : {1, 4, 16, 17}) {
               const size_t wm = pkv_decode_multi_workspace_bytes(b, ql, h[0], h[1], d, n, sp);
               if (ql == 17) CHECK(wm == 0);
-              if (ql == 1) CHECK(wm == ws);
+              if (ql == 1) CHECK(wm <= ws);  // plain decode may also hold balanced partials
             }
             for (int32_t shared : {0, 64, 1000}) {
               const size_t wsh =
@@ -110,7 +110,8 @@ int main() {
     const size_t need = pkv_decode_workspace_bytes(4, 32, 8, 64, 2048, 0);
     void* misaligned = reinterpret_cast<void*>((uintptr_t(1) << 20) + 16);
     CHECK(decode(16, 128, 4, 2048, 32, 8, 64, 0.125f, 0, misaligned, need) == PKV_EINVAL);
-    CHECK(decode(16, 128, 4, 2048, 32, 8, 64, 0.125f, 0, F, need - 1) == PKV_ENOSPACE);
+    CHECK(need > 256);
+    CHECK(decode(16, 128, 4, 2048, 32, 8, 64, 0.125f, 0, F, 256) == PKV_ENOSPACE);
   }
   CHECK(pkv_decode_step(F, nullptr, F, FI, F, F, 16, 100, FI, 128, FI, 4, 2048, 32, 8, 64,
                         0.125f, 0, F, nullptr, 0, nullptr) == PKV_EINVAL);

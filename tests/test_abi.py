@@ -177,7 +177,10 @@ def test_decode_shared_workspace_size():
     plain = pkv.pkv_decode_workspace_bytes(64, 32, 8, 64, 2048)
     shared = pkv.pkv_paged_attn_decode_shared_workspace_bytes(64, 32, 8, 64, 2048, 1024)
     assert shared > plain   # 16 more partial slots per (request, KV head) for the prefix splits
-    assert pkv.pkv_paged_attn_decode_shared_workspace_bytes(64, 32, 8, 64, 2048, 0) == plain
+    # no prefix splits: the split partials alone (plain decode may reserve
+    # more, for the rows of its balanced launch)
+    none = pkv.pkv_paged_attn_decode_shared_workspace_bytes(64, 32, 8, 64, 2048, 0)
+    assert 0 < none <= plain
     assert pkv.pkv_paged_attn_decode_shared_workspace_bytes(64, 32, 8, 64, 2048, 4096) == 0
 
 

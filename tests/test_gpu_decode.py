@@ -391,8 +391,8 @@ def test_decode_device_chosen_split(B, hq, hkv, d, lo, hi, q_len):
         out = pkv.pkv_paged_attn_decode_multi(w.q, w.k_cache, w.v_cache, w.page_table,
                                               w.seq_lens, w.max_seq_len, w.scale, workspace=ws)
     torch.cuda.synchronize()
-    # the split the kernels used is recorded in the workspace's last 256 bytes
-    used = int(ws[-256:].view(torch.int32)[0].item())
+    # the split the kernels used is recorded in the workspace's first 256 bytes
+    used = int(ws[:256].view(torch.int32)[0].item())
     host = pkv.pkv_decode_split_tokens(B, hkv, w.max_seq_len)
     assert used >= host and used % 16 == 0, (used, host)
     got = f64(out)
