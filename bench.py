@@ -152,7 +152,9 @@ def segment_trace(path: str, gap_ms: float = 20.0):
     with open(path, newline="") as fh:
         for r in csv.DictReader(fh):
             by[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
-    keep = ("prefill_kernel", "decode_split_kernel", "decode_combine_kernel", "store_kv_kernel")
+    keep = ("prefill_kernel", "decode_split_kernel", "decode_combine_kernel",
+            "decode_balanced_kernel", "decode_combine_balanced_kernel", "decode_split_prefix_kernel",
+            "store_kv_kernel")
     for name, v in by.items():
         short = next((k for k in keep if k in name), None)
         if short is None:
