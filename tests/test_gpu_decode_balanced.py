@@ -17,7 +17,9 @@ from paged_kv_attention_out_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-MAX_RESIDENT_WAVES = 4096  # above any round of the decode kernels on this GPU
+# Units of max-length requests at or above 4 x 4096 (eight rounds of the
+# 2,048 decode waves resident on this GPU) always take several rounds.
+MAX_RESIDENT_WAVES = 4096
 
 
 def _lengths(B, lo, hi, seed):
@@ -51,6 +53,7 @@ CASES = [
     (48, 8, 1, 128, 32, 20000, 60000),
     (200, 4, 2, 64, 64, 100, 6000),
     (40, 16, 4, 64, 128, 4000, 30000),
+    (256, 8, 8, 64, 16, 2000, 12000),   # one query head per KV head, the most requests
 ]
 
 
@@ -61,7 +64,7 @@ def test_balanced_decode(B, hq, hkv, d, ps, lo, hi):
     # units of max-length requests at the host split, over KV heads: beyond
     # four rounds of any resident wave count, so no one-round launch
     worst = B * (-(-int(lens.max()) // split)) * hkv
-    assert worst > 4 * MAX_RESIDENT_WAVES, "batch too small for several rounds"
+    assert worst >= 4 * MAX_RESIDENT_WAVES, "batch too small for several rounds"
     units = worst
     w = inputs.build_decode(B, hq, hkv, d, ps, lens, seed=B + d, device="cuda")
     w.seq_lens[2] = -3  # a negative length reads nothing and gives a zero row
@@ -90,3 +93,60 @@ def test_balanced_decode_step_fused_store():
     assert np.array_equal(inputs.bf16_bits(w.k_cache), kc_ref), "K pool differs from the store"
     assert np.array_equal(inputs.bf16_bits(w.v_cache), vc_ref), "V pool differs from the store"
     print("max/mean err per 16 requests", _check(w, out))
+
+
+def test_split_launch_beyond_256_requests():
+    """257 requests: more than the balanced launch keeps in registers, so the
+    split launch runs the several rounds; same checks."""
+    B, hq, hkv, d, ps = 257, 16, 8, 64, 16
+    lens = _lengths(B, 500, 3000, seed=257)
+    w = inputs.build_decode(B, hq, hkv, d, ps, lens, seed=17, device="cuda")
+    w.seq_lens[2] = -3
+    out = pkv.pkv_paged_attn_decode(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens,
+                                    w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    print("max/mean err per 16 requests", _check(w, out))
+
+
+def test_balanced_step_noalloc_and_graph_match_the_workspace_call():
+    """A multi-round decode step through the fixed scratch and through a
+    captured graph gives the same bits as the call with a workspace."""
+    B, hq, hkv, d, ps = 100, 16, 8, 128, 256
+    lens = np.random.default_rng(3).integers(1000, 9001, size=B).astype(np.int32)
+    w = inputs.build_decode(B, hq, hkv, d, ps, lens, seed=21, device="cuda", store_new=True)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+
+    def restore():
+        w.k_cache.copy_(k0)
+        w.v_cache.copy_(v0)
+
+    ws = pkv.decode_workspace(B, hq, hkv, d, w.max_seq_len)
+    out_a = pkv.pkv_decode_step(w.q, w.k_new, w.v_new, w.out_loc, w.k_cache, w.v_cache,
+                                w.page_table, w.seq_lens, w.max_seq_len, w.scale, workspace=ws)
+    ka = w.k_cache.clone()
+    restore()
+    out_b = torch.full_like(w.q, 3.0)
+    pkv.pkv_decode_step_noalloc(w.q, w.k_new, w.v_new, w.out_loc, w.k_cache, w.v_cache,
+                                w.page_table, w.seq_lens, w.max_seq_len, w.scale, out=out_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    assert torch.equal(ka.view(torch.int16), w.k_cache.view(torch.int16))
+    out_g = torch.empty_like(w.q)
+    gws = torch.zeros(pkv.pkv_decode_graphs_workspace_bytes([B], hq, hkv, d, w.max_seq_len),
+                      dtype=torch.uint8, device="cuda")
+    graphs = pkv.pkv_decode_graphs_create([B], w.q, w.k_cache, w.v_cache, w.page_table,
+                                          w.seq_lens, w.max_seq_len, w.scale, out_g,
+                                          k_new=w.k_new, v_new=w.v_new, out_loc=w.out_loc,
+                                          workspace=gws)
+    try:
+        for _ in range(3):
+            restore()
+            out_g.fill_(7.0)
+            torch.cuda.synchronize()
+            assert graphs.replay(B) == B
+            torch.cuda.synchronize()
+            assert torch.equal(out_a.view(torch.int16), out_g.view(torch.int16))
+            assert torch.equal(ka.view(torch.int16), w.k_cache.view(torch.int16))
+    finally:
+        graphs.destroy()
+    print("max/mean err per 16 requests", _check(w, out_a))
