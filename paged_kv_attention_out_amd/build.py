@@ -74,7 +74,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
 def code_objects():
     """Unbundle the gfx950 code object of every compiled source (for ISA
-    checks of what this build produced); returns their paths."""
+    checks of what the last compile produced); returns their paths."""
     llvm = "/opt/rocm/llvm/bin"
     paths = []
     for src in sources():

@@ -1,4 +1,4 @@
-"""Checks on the AMD assembly of the code objects this build produced.
+"""Checks on the AMD assembly of the code objects compiled from this source tree.
 
 * No instruction writes through the scalar data cache (scalar stores,
   scalar atomics, scalar cache write-back / discard): every store and
