@@ -232,6 +232,10 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
         ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
         cu_g = torch.tensor([0, B], dtype=torch.int32, device="cuda")
         sh_l = torch.full((B,), shared_len, dtype=torch.int32, device="cuda")
+    if is_decode and ws is not None and ws.numel() >= 256:
+        # the split kernel writes the split it used to the first word; the
+        # balanced launch (no fixed split) leaves this marker
+        ws[:4].view(torch.int32).fill_(-1)
     ws_ptr, ws_bytes = (0, 0) if ws is None else (ws.data_ptr(), ws.numel())
 
     # Pre-marshalled C calls: the timed loop only enqueues.
@@ -314,11 +318,14 @@ def time_workload(name: str, steps: int, warmup: int, split_tokens: int = 0,
             raise RuntimeError(f"{name}: non-finite output")
     if R > 1 and not torch.equal(calls[0][2], calls[1][2]):
         raise RuntimeError(f"{name}: replicas disagree")
-    # the split the kernels used: recorded by the split kernel in the last
-    # 256-byte slot of the decode workspace (the device may pick a longer one)
+    # the split the kernels used: recorded by the split kernel in the first
+    # word of the decode workspace (the device may pick a longer one); the
+    # balanced launch shares each KV head's blocks evenly instead
+    launch = None
     if is_decode and ws is not None and ws.numel() >= 256:
-        split = int(ws[-256:].view(torch.int32)[0].item())
-    res = dict(workload=w, replicas=R, split=split, fused=fused,
+        rec = int(ws[:4].view(torch.int32)[0].item())
+        split, launch = (None, "balanced") if rec < 0 else (rec, "split")
+    res = dict(workload=w, replicas=R, split=split, launch=launch, fused=fused,
                ms_per_step=(t1 - t0) * 1e3 / steps,
                kernel_ms_mean=float(np.mean(kernel_ms)), kernel_ms_median=float(np.median(kernel_ms)),
                kernel_ms_min=float(np.min(kernel_ms)))
@@ -772,7 +779,7 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "page_size": w.page_size,
                    "seq_lens_sum": int(w.seq_lens_np.sum()), "seed": w.seed,
-                   "replicas": r["replicas"], "split_tokens": r["split"],
+                   "replicas": r["replicas"], "split_tokens": r["split"], "launch": r["launch"],
                    "step": ("pkv_decode_step (store_kv fused into paged decode)" if r["fused"]
                             else "pkv_store_kv + pkv_paged_attn_decode"),
                    "parallelism": "single GPU"},
@@ -800,7 +807,8 @@ def main():
                               "kernel_us_mean": round(a["kernel_ms_mean"] * 1e3, 2),
                               "ms_per_step": round(a["ms_per_step"], 4),
                               "tokens_per_s": round(wa.num_seqs / (a["ms_per_step"] * 1e-3), 1),
-                              "split_tokens": a["split"], "replicas": a["replicas"]}
+                              "split_tokens": a["split"], "launch": a["launch"],
+                              "replicas": a["replicas"]}
                 if name == "shared_prefix_decode":
                     # counting rule: shared pages count once per request; the
                     # distinct K/V bytes of the batch are far fewer
@@ -845,7 +853,8 @@ def main():
                                "ms_per_step": round(a["ms_per_step"], 4),
                                "query_tokens_per_s":
                                    round(wa.num_tokens / (a["ms_per_step"] * 1e-3), 1),
-                               "split_tokens": a["split"], "replicas": a["replicas"]}
+                               "split_tokens": a["split"], "launch": a["launch"],
+                              "replicas": a["replicas"]}
         del a, wa
         torch.cuda.empty_cache()
         a = time_workload("spec_decode", max(10, args.steps // 10), max(3, args.warmup // 4),

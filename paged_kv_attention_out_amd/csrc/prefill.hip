@@ -16,7 +16,9 @@
 // longest key ranges first.  The hardware dispatcher starts
 // blocks strictly in grid order, so a grid of one block per item leaves CUs
 // idle behind long-running blocks; pulling keeps every resident block busy
-// until the items run out.  The block that draws the last ticket puts the
+// until the items run out.  A block draws its next ticket as the last tile
+// of its current item ends, so the last (shortest) items go to the blocks
+// that free up first.  The block that draws the last ticket puts the
 // counter back to zero, ready for the next call on the same workspace.
 //
 // Per 64-key tile:
@@ -111,8 +113,9 @@ __device__ __forceinline__ void request_geometry(const PrefillParams& p, int r, 
 }
 
 template <int D, int NB, int G, typename KV>
-__device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int r, int kvh,
-                                            int tid, int lane, int wave, KV& kv);
+__device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int r, int kvh,
+                                            int tid, int lane, int wave, KV& kv,
+                                            uint32_t& next, const int (&geo)[3][64]);
 
 template <int D, int NB, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
@@ -123,6 +126,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   // [buffer][K or V][row * pitch + dim]: two tiles in flight, one barrier per tile.
   __shared__ __attribute__((aligned(16))) uint16_t kv[2][2][TILE];
   __shared__ uint32_t item_slot[2];
+  __shared__ int geo[3][64];  // longest-first: first new token, new tokens, prefix per request
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,10 +141,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   // from the last, which leaves the tiles of long prefixes for the end.
   int lv_b = 0, lv_n = 0;     // this lane's request: first level, tile count
   int level = -1, below = 0;  // walk state: current level, tickets above it
+  // Tickets at or past n_end end a block.  In longest-first order every
+  // ticket below the tile count times the KV heads is a real item, so the
+  // blocks stop there rather than draw the empty query tiles one by one.
+  uint32_t n_end = (uint32_t)p.n_items;
+  // Wave 0 also puts every request's geometry in LDS, so an item reads it
+  // there instead of making a round trip to memory.
   if (p.longest_first) {
     if (lane < p.num_seqs) {
       int s0r, Lr, Pr;
       request_geometry(p, lane, s0r, Lr, Pr);
+      if (wave == 0) {
+        geo[0][lane] = s0r;
+        geo[1][lane] = Lr;
+        geo[2][lane] = Pr;
+      }
       lv_b = Pr / QT;
       lv_n = (Lr + QT - 1) / QT;
     }
@@ -148,23 +163,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) top = max(top, __shfl_xor(top, off));
     level = uniform(top);
+    int tot = lv_n;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+    n_end = (uint32_t)uniform(tot) * (uint32_t)p.num_kv_heads;
   }
 
   // Tickets are compared unsigned, so even a counter left non-zero by a
-  // misuse only ever yields item numbers inside [0, n_items).
+  // misuse only ever yields item numbers inside [0, n_end).
   if (tid == 0) item_slot[0] = atomicAdd(p.counter, 1u);
   __syncthreads();
   int par = 0;
   // readfirstlane: the item is block-uniform, so its geometry stays scalar.
   for (uint32_t item = uniform(item_slot[0]);; item = uniform(item_slot[par])) {
-    if (item >= (uint32_t)p.n_items) {
+    if (item >= n_end) {
       // Every block draws exactly one ticket past the end; the last such
       // ticket is drawn after all others, so its holder resets the counter.
-      if (tid == 0 && item - (uint32_t)p.n_items == gridDim.x - 1) atomicExch(p.counter, 0u);
+      if (tid == 0 && item - n_end == gridDim.x - 1) atomicExch(p.counter, 0u);
       break;
     }
-    if (tid == 0) item_slot[par ^ 1] = atomicAdd(p.counter, 1u);
-    par ^= 1;
     int qt, r, kvh;
     if (p.longest_first) {
       const int t = (int)item / p.num_kv_heads;
@@ -193,14 +210,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       r = (int)item % rk_all / p.num_kv_heads;
       kvh = (int)item % p.num_kv_heads;
     }
-    if (qt >= 0) attend_item<D, NB, G>(p, qt, r, kvh, tid, lane, wave, kv);
+    // The next ticket is drawn inside the item, after its last tile (thread
+    // 0 only); an item with no positions draws it here.
+    uint32_t next = 0;
+    const bool drawn = qt >= 0 && attend_item<D, NB, G>(p, qt, r, kvh, tid, lane, wave, kv, next, geo);
+    if (tid == 0) item_slot[par ^ 1] = drawn ? next : atomicAdd(p.counter, 1u);
+    par ^= 1;
     __syncthreads();  // LDS tiles free; the next item number is visible
   }
 }
 
+// Returns false (drawing nothing) for an item with no positions; else thread
+// 0 has drawn the block's next ticket into `next`.
 template <int D, int NB, int G, typename KV>
-__device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int r, int kvh,
-                                            int tid, int lane, int wave, KV& kv) {
+__device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int r, int kvh,
+                                            int tid, int lane, int wave, KV& kv,
+                                            uint32_t& next, const int (&geo)[3][64]) {
   constexpr int QT = 128 * NB / G;        // positions per item
   constexpr int KS = D / 16;              // 16-dim steps of QK^T
   constexpr int DB = D / 32;              // 32-dim blocks of the output
@@ -210,9 +235,15 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
   constexpr int LOADS = kKeys / ROWS;     // passes per tile
 
   int s0, L, P;
-  request_geometry(p, r, s0, L, P);
+  if (p.longest_first) {
+    s0 = uniform(geo[0][r]);
+    L = uniform(geo[1][r]);
+    P = uniform(geo[2][r]);
+  } else {
+    request_geometry(p, r, s0, L, P);
+  }
   const int q0 = qt * QT;
-  if (q0 >= L) return;
+  if (q0 >= L) return false;
   const int qlast = min(q0 + QT, L) - 1;
   const int kend = P + qlast + 1;   // keys [0, kend) are read
   const int kfull = P + q0 + 1;     // keys [0, kfull) are visible to every column
@@ -525,6 +556,18 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
     if (kt + 1 < ntiles) tile(kt + 1, Set1{});
   }
 
+  // The block's next ticket, drawn as its last tile ends: the last tickets
+  // go to the blocks that free up first.  The result is stored to LDS only
+  // after the output below, so the round trip overlaps it; the opaque zero
+  // keeps the address lane-varying in the compiler's eyes, since a
+  // uniform-address atomic is rewritten as a wave reduction that waits for
+  // its result (and every older load) right where it is issued.
+  if (tid == 0) {
+    int zero = 0;
+    asm volatile("" : "+v"(zero));
+    next = atomicAdd(p.counter + zero, 1u);
+  }
+
   // Normalise and write the valid columns: lane holds dims
   // db*32 + 8*(v/4) + 4*half + v%4 of its column.
 #pragma unroll
@@ -543,6 +586,7 @@ __device__ __forceinline__ void attend_item(const PrefillParams& p, int qt, int 
         *reinterpret_cast<uint2*>(op + db * 32 + 8 * v4 + 4 * half) = w;
       }
   }
+  return true;
 }
 
 // Resident blocks per CU of one instantiation times the CU count of the
