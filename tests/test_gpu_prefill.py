@@ -225,3 +225,20 @@ def test_prefill_long_prefix_query_tile_order():
     out = run_prefill(w)
     torch.cuda.synchronize()
     print(assert_close(f64(out), ref, "long prefix"))
+
+
+@pytest.mark.parametrize("prefix", [[30000, 20000, 10], [40000, 30000, 5]],
+                         ids=["3136_pages", "4386_pages"])
+def test_prefill_long_prefixes(prefix):
+    # Head_dim 64, longest-first order over several hundred levels: long
+    # cached prefixes with few new tokens, thousands of page numbers per
+    # call, and a near-empty request beside them.
+    qlens = [40, 70, 30]
+    w = inputs.build_prefill(3, 8, 2, 64, 16, prefix, qlens, seed=93 + prefix[0], device="cuda")
+    pages = sum(-(-(p + q) // 16) for p, q in zip(prefix, qlens))
+    print(f"prefill long prefixes: pages={pages}", flush=True)
+    ref = _oracle(w)
+    run_store(w)
+    out = run_prefill(w)
+    torch.cuda.synchronize()
+    print(pages, assert_close(f64(out), ref, f"long prefixes, {pages} pages"))
