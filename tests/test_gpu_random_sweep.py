@@ -137,3 +137,71 @@ def test_random_prefill(i):
     out = run_prefill(w)
     torch.cuda.synchronize()
     print(i, assert_close(f64(out), ref, f"random prefill {i}"))
+
+
+N_SHARED = 16
+N_LARGE = 8
+
+
+def _shared_case(i):
+    rng = np.random.default_rng(11000 + i)
+    hq, hkv, d, ps = _heads(rng)
+    groups = [(int(rng.integers(1, 41)), int(rng.integers(0, 1501)))
+              for _ in range(int(rng.integers(1, 5)))]
+    return hq, hkv, d, ps, groups, bool(rng.random() < 0.5), _split(rng)
+
+
+@pytest.mark.parametrize("i", range(N_SHARED))
+def test_random_decode_shared(i):
+    from test_gpu_decode_shared import _grouped, _run
+    hq, hkv, d, ps, groups, store, split = _shared_case(i)
+    print(f"random shared {i}: hq={hq} hkv={hkv} d={d} ps={ps} groups={groups} "
+          f"store={store} split={split}", flush=True)
+    w, cu, shared, max_group, max_shared = _grouped(hq, hkv, d, ps, groups, 12000 + i, store)
+    kc, vc = host_pools(w)
+    ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale)
+    out = _run(w, cu, shared, max_group, max_shared, split)
+    torch.cuda.synchronize()
+    print(i, assert_close(f64(out), ref, f"random shared {i}"))
+
+
+def _large_case(i):
+    # Batches long enough to need several rounds of units (the balanced
+    # launch when it applies); a random subset of requests is compared.
+    rng = np.random.default_rng(13000 + i)
+    hq, hkv, d, ps = _heads(rng)
+    hkv = max(hkv, 2)
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(64, 257))
+    lens = [int(x) for x in rng.integers(1, 8193, B)]
+    lens[int(rng.integers(0, B))] = 8192
+    for r in rng.choice(B, size=min(3, B), replace=False):
+        lens[int(r)] = int(rng.choice([0, 1, 16, 17]))
+    reqs = sorted(int(r) for r in rng.choice(B, size=24, replace=False))
+    return hq, hkv, d, ps, lens, reqs, bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_decode_large(i):
+    hq, hkv, d, ps, lens, reqs, step = _large_case(i)
+    if step:
+        lens = [max(n, 1) for n in lens]
+    print(f"random large {i}: hq={hq} hkv={hkv} d={d} ps={ps} B={len(lens)} "
+          f"sum={sum(lens)} step={step}", flush=True)
+    w = inputs.build_decode(len(lens), hq, hkv, d, ps, lens, seed=14000 + i, device="cuda",
+                            store_new=step)
+    kc, vc = host_pools(w)
+    live = [r for r in reqs if lens[r] > 0]
+    ref = orc.decode(inputs.bf16_bits(w.q), kc, vc, w.page_table_np, w.seq_lens_np, w.scale,
+                     requests=live)
+    if step:
+        out = pkv.pkv_decode_step(w.q, w.k_new, w.v_new, w.out_loc, w.k_cache, w.v_cache,
+                                  w.page_table, w.seq_lens, w.max_seq_len, w.scale)
+    else:
+        out = run_decode(w)
+    torch.cuda.synchronize()
+    got = f64(out)
+    print(i, assert_close(got, ref, f"random large {i}"))
+    for r in reqs:
+        if lens[r] == 0:
+            assert (got[r] == 0).all(), f"request {r} without keys must get zeros"
