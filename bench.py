@@ -492,8 +492,28 @@ def time_metadata(steps: int):
             fn()
             b.record()
         torch.cuda.synchronize()
+        # Events around single calls of a few-microsecond kernel time the
+        # host's launch rate; device time per call comes from a captured
+        # graph of back-to-back calls, replayed between two events.
+        per_graph = 20
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(5, steps // per_graph)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
         res[name] = {"us_mean": round(float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3,
-                                      2)}
+                                      2),
+                     "device_us_per_call": round(e0.elapsed_time(e1) * 1e3 / (reps * per_graph),
+                                                 2)}
+        del g
     res["prefill_metadata"]["tokens"] = wp.num_tokens
     res["decode_metadata"]["requests"] = wd.num_seqs
     if not (torch.equal(cu, wp.cu_seqlens_q) and torch.equal(loc_p, wp.out_loc)

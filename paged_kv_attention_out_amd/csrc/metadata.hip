@@ -15,6 +15,8 @@
 // page_size + t % page_size (mini-sglang "Engine Class", Key Attributes:
 // page_table; miniVLLM allocate_kv_cache for the pool layout).
 
+#include <algorithm>
+
 #include "pkv_common.h"
 
 namespace {
@@ -84,14 +86,21 @@ __global__ __launch_bounds__(kScanThreads) void prefill_cu_kernel(PrefillMetaPar
   }
 }
 
-// Batches of up to kScanThreads requests in one launch: the workgroup scans
-// the counts as above, keeps the offsets in LDS, then each wave writes the
-// slots of every 16th request.
+// Batches of up to kScanThreads requests in one launch.  Every workgroup
+// scans the counts as above and keeps each request's end offset and first
+// position in LDS; then the grid strides over the batch's new tokens, each
+// thread finding its token's request by binary search over the offsets, so
+// the slots of one long request are spread over the whole grid instead of
+// one wave's serial loop.  Workgroup 0 writes cu_seqlens.
+constexpr int kMetaBlocks = 64;  // grid bound of the small-batch builder
+
 __global__ __launch_bounds__(kScanThreads) void prefill_meta_small_kernel(PrefillMetaParams p) {
   __shared__ int buf[2][kScanThreads];
+  __shared__ int first_pos[kScanThreads];
   const int tid = threadIdx.x;
   const int r = tid;
   const int cnt = r < p.num_seqs ? new_tokens(p, r) : 0;
+  first_pos[tid] = r < p.num_seqs ? max(p.prefix_lens[r], 0) : 0;
   int cur = 0;
   buf[0][tid] = cnt;
   __syncthreads();
@@ -101,21 +110,21 @@ __global__ __launch_bounds__(kScanThreads) void prefill_meta_small_kernel(Prefil
     cur ^= 1;
     __syncthreads();
   }
-  if (tid == 0) p.cu_seqlens[0] = 0;
-  if (r < p.num_seqs) p.cu_seqlens[r + 1] = buf[cur][tid];
-  if (p.max_tokens == 0) return;
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int q = wave; q < p.num_seqs; q += kScanThreads / 64) {
-    const int end = buf[cur][q];
-    const int len = q < p.num_seqs ? new_tokens(p, q) : 0;
-    const int start = end - len;
+  const int* end = buf[cur];  // end[q]: new tokens of requests 0..q
+  if (blockIdx.x == 0) {
+    if (tid == 0) p.cu_seqlens[0] = 0;
+    if (r < p.num_seqs) p.cu_seqlens[r + 1] = end[tid];
+  }
+  const int total = min(end[kScanThreads - 1], p.max_tokens);
+  for (int t = blockIdx.x * kScanThreads + tid; t < total; t += gridDim.x * kScanThreads) {
+    // the first request whose end offset exceeds t
+    int q = 0;
+#pragma unroll
+    for (int step = kScanThreads / 2; step >= 1; step >>= 1)
+      if (end[q + step - 1] <= t) q += step;
+    const int start = q == 0 ? 0 : end[q - 1];
     const int32_t* row = p.page_table + (int64_t)q * p.pt_stride;
-    const int first = max(p.prefix_lens[q], 0);
-    for (int i = lane; i < len; i += 64) {
-      const int t = start + i;
-      if (t >= p.max_tokens) break;
-      p.out_loc[t] = slot_of(row, p.pt_stride, p.page_size, first + i);
-    }
+    p.out_loc[t] = slot_of(row, p.pt_stride, p.page_size, first_pos[q] + (t - start));
   }
 }
 
@@ -169,8 +178,12 @@ extern "C" int pkv_prefill_metadata(const int32_t* seq_lens, const int32_t* pref
   p.page_size = page_size;
   p.max_tokens = max_tokens;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (num_seqs <= kScanThreads)
-    return launch(prefill_meta_small_kernel, dim3(1), dim3(kScanThreads), s, p);
+  if (num_seqs <= kScanThreads) {
+    const int blocks = (int)std::min<int64_t>(
+        std::max<int64_t>(((int64_t)max_tokens + kScanThreads - 1) / kScanThreads, 1),
+        kMetaBlocks);
+    return launch(prefill_meta_small_kernel, dim3((unsigned)blocks), dim3(kScanThreads), s, p);
+  }
   const int st = launch(prefill_cu_kernel, dim3(1), dim3(kScanThreads), s, p);
   if (st != PKV_OK || max_tokens == 0) return st;
   return launch(prefill_slots_kernel, dim3((unsigned)num_seqs), dim3(256), s, p);
