@@ -363,8 +363,30 @@ def time_store(name: str, steps: int, warmup: int):
         ev[i][1].record()
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # device time per call: a captured graph of back-to-back calls (the
+    # events above also time the host's launch rate when a call is short)
+    per_graph = 20
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for i in range(per_graph):
+            if f(*(calls[i % R][2][:-1] + (cs,))) != 0:
+                raise RuntimeError("pkv_store_kv failed")
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(5, steps // per_graph)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    dev_ms = e0.elapsed_time(e1) / (reps * per_graph)
+    del g
     return {"rows": T, "us_mean": round(ms * 1e3, 2), "bytes": nbytes,
-            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "device_us_per_call": round(dev_ms * 1e3, 2),
+            "device_GB/s": round(nbytes / (dev_ms * 1e-3) / 1e9, 1)}
 
 
 def time_graph_buckets(name: str, steps: int, warmup: int,
