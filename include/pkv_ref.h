@@ -2,7 +2,7 @@
  * pkv_ref.h -- measurement reference shipped beside the attention library
  * (libpkv.so).  Not part of the attention path: the benchmark uses it to
  * measure the device's plain streaming-read rate over the same byte counts
- * the decode calls read, the floor the decode kernels are judged against.
+ * the decode calls read, the floor the decode kernels are compared with.
  *
  * Status codes are those of pkv.h.
  */

@@ -1,5 +1,5 @@
 // HBM read-rate reference: a plain streaming read of a contiguous buffer,
-// the floor against which the decode kernels' byte rate is judged.  It is
+// the floor against which the decode kernels' byte rate is compared.  It is
 // not part of the attention path; the benchmark times it over the same byte
 // counts the decode calls read.
 //
