@@ -70,6 +70,7 @@ struct PrefillParams {
   int32_t longest_first;  // 1: tickets map to (request, query tile) pairs longest first
   uint32_t num_pages_u32;  // min(num_pages, 2^31 - 1); larger page numbers read its last page
   uint32_t page_bytes;     // bytes per page of one pool (K or V)
+  uint32_t pool_bytes;     // bytes of one pool when they fit 32 bits (buffer loads), else 0
   uint32_t row_bytes;      // bytes per token row (all KV heads)
   float scale_log2;
 };
@@ -80,6 +81,8 @@ constexpr float kTau = 8.0f;
 constexpr float kPmax = 256.0f;
 static_assert(kPmax == (float)(1 << (int)kTau), "kPmax is 2^kTau");
 constexpr int kKeys = 64;  // keys per tile
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle.
+constexpr int kBufferFlags = 0x00020000;
 
 // fmax over lanes l and l ^ 32 (the two halves of one 32x32 accumulator column).
 __device__ __forceinline__ float max_xor32(float x) {
@@ -112,12 +115,16 @@ __device__ __forceinline__ void request_geometry(const PrefillParams& p, int r, 
   P = min(max(p.prefix_lens[r], 0), p.max_seq_len - L);
 }
 
-template <int D, int NB, int G, typename KV>
+template <int D, int NB, int G, bool BUF, typename KV>
 __device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int r, int kvh,
                                             int tid, int lane, int wave, KV& kv,
                                             uint32_t& next, const int (&geo)[3][64]);
 
-template <int D, int NB, int G>
+// BUF: the pools are below 4 GiB and their pages and page numbers below 2^24,
+// so rows are fetched by buffer loads at 32-bit offsets from the pool bases
+// (one 24-bit multiply-add per row instead of 64-bit address arithmetic;
+// offsets past the pool read zeros).
+template <int D, int NB, int G, bool BUF>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   constexpr int QT = 128 * NB / G;
   constexpr int TILE = kKeys * (D + 8);
@@ -213,7 +220,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     // The next ticket is drawn inside the item, after its last tile (thread
     // 0 only); an item with no positions draws it here.
     uint32_t next = 0;
-    const bool drawn = qt >= 0 && attend_item<D, NB, G>(p, qt, r, kvh, tid, lane, wave, kv, next, geo);
+    const bool drawn = qt >= 0 && attend_item<D, NB, G, BUF>(p, qt, r, kvh, tid, lane, wave, kv, next,
+                                                                 geo);
     if (tid == 0) item_slot[par ^ 1] = drawn ? next : atomicAdd(p.counter, 1u);
     par ^= 1;
     __syncthreads();  // LDS tiles free; the next item number is visible
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 
 // Returns false (drawing nothing) for an item with no positions; else thread
 // 0 has drawn the block's next ticket into `next`.
-template <int D, int NB, int G, typename KV>
+template <int D, int NB, int G, bool BUF, typename KV>
 __device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int r, int kvh,
                                             int tid, int lane, int wave, KV& kv,
                                             uint32_t& next, const int (&geo)[3][64]) {
@@ -298,14 +306,26 @@ __device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int 
   // arithmetic (the last tile of an item takes the general path).
   const bool small_pages = p.page_size <= kKeys;
   const int pstep = kKeys >> p.page_shift;
-  const char* kin[LOADS];
+  // kin: row addresses (BUF: byte offsets) within a page, per row slot
+  std::conditional_t<BUF, uint32_t, const char*> kin[LOADS];
   int pidx0[LOADS];
+  const uint32_t hoff = (uint32_t)(kvh * D + lpc * 8) * 2u;  // BUF: the head's slice
 #pragma unroll
   for (int it = 0; it < LOADS; ++it) {
     const int r0 = lrow + ROWS * it;
-    kin[it] = kbase + __umul24(r0 & pmask, p.row_bytes);
+    if constexpr (BUF)
+      kin[it] = hoff + __umul24(r0 & pmask, p.row_bytes);
+    else
+      kin[it] = kbase + __umul24(r0 & pmask, p.row_bytes);
     pidx0[it] = r0 >> p.page_shift;
   }
+  // BUF: 16 bytes of pool `pool` (K or V) at a byte offset
+  auto bload = [&](const uint16_t* pool, uint32_t off) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(pool), (short)0, (int)p.pool_bytes, kBufferFlags);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
   auto whole = [&](int kt) { return small_pages && kt * kKeys + kKeys - 1 <= klast; };
   auto fetch_pages = [&](int kt) {
     if (whole(kt)) {
@@ -327,20 +347,33 @@ __device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int 
     if (whole(kt)) {
 #pragma unroll
       for (int it = 0; it < LOADS; ++it) {
-        const uint32_t page = min((uint32_t)pg[it], p.num_pages_u32 - 1u);
-        const char* kp = kin[it] + (uint64_t)page * p.page_bytes;
-        kr[set][it] = ld16(kp);
-        vr[set][it] = ld16(kp + v_minus_k);
+        if constexpr (BUF) {
+          const uint32_t off = __umul24((uint32_t)pg[it], p.page_bytes) + kin[it];
+          kr[set][it] = bload(p.k_cache, off);
+          vr[set][it] = bload(p.v_cache, off);
+        } else {
+          const uint32_t page = min((uint32_t)pg[it], p.num_pages_u32 - 1u);
+          const char* kp = kin[it] + (uint64_t)page * p.page_bytes;
+          kr[set][it] = ld16(kp);
+          vr[set][it] = ld16(kp + v_minus_k);
+        }
       }
     } else {
 #pragma unroll
       for (int it = 0; it < LOADS; ++it) {
         const int kg = min(kt * kKeys + lrow + ROWS * it, klast);
-        const uint32_t page = min((uint32_t)pg[it], p.num_pages_u32 - 1u);
-        const char* kp =
-            kbase + (uint64_t)page * p.page_bytes + __umul24(kg & pmask, p.row_bytes);
-        kr[set][it] = ld16(kp);
-        vr[set][it] = ld16(kp + v_minus_k);
+        if constexpr (BUF) {
+          const uint32_t off = __umul24((uint32_t)pg[it], p.page_bytes) + hoff +
+                               __umul24(kg & pmask, p.row_bytes);
+          kr[set][it] = bload(p.k_cache, off);
+          vr[set][it] = bload(p.v_cache, off);
+        } else {
+          const uint32_t page = min((uint32_t)pg[it], p.num_pages_u32 - 1u);
+          const char* kp =
+              kbase + (uint64_t)page * p.page_bytes + __umul24(kg & pmask, p.row_bytes);
+          kr[set][it] = ld16(kp);
+          vr[set][it] = ld16(kp + v_minus_k);
+        }
       }
     }
   };
@@ -633,7 +666,7 @@ __device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int 
 
 // Resident blocks per CU of one instantiation times the CU count of the
 // current device, computed once per (device, instantiation).
-template <int D, int NB, int G>
+template <int D, int NB, int G, bool BUF>
 int resident_blocks() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cache[kMaxDevices];
@@ -647,19 +680,26 @@ int resident_blocks() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(prefill_kernel<D, NB, G>), 256, 0) != hipSuccess)
+          &per_cu, reinterpret_cast<const void*>(prefill_kernel<D, NB, G, BUF>), 256, 0) !=
+      hipSuccess)
     return 0;
   const int n = cus * per_cu;
   if (n > 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
-template <int D, int NB, int G>
-int launch_prefill(PrefillParams& p, hipStream_t s) {
-  const int resident = resident_blocks<D, NB, G>();
+template <int D, int NB, int G, bool BUF>
+int launch_prefill_as(PrefillParams& p, hipStream_t s) {
+  const int resident = resident_blocks<D, NB, G, BUF>();
   if (resident <= 0) return PKV_EHIP;
   const int grid = (int)std::min<int64_t>(p.n_items, resident);
-  return pkv_host::launch(prefill_kernel<D, NB, G>, dim3((unsigned)grid), dim3(256), s, p);
+  return pkv_host::launch(prefill_kernel<D, NB, G, BUF>, dim3((unsigned)grid), dim3(256), s, p);
+}
+
+template <int D, int NB, int G>
+int launch_prefill(PrefillParams& p, hipStream_t s) {
+  return p.pool_bytes != 0 ? launch_prefill_as<D, NB, G, true>(p, s)
+                           : launch_prefill_as<D, NB, G, false>(p, s);
 }
 
 }  // namespace
@@ -733,6 +773,11 @@ extern "C" int pkv_paged_attn_prefill(const void* q, const int32_t* cu_seqlens_q
   p.num_pages_u32 = (uint32_t)std::min<int64_t>(num_pages, INT32_MAX);
   p.row_bytes = (uint32_t)(num_kv_heads * head_dim * 2);
   p.page_bytes = (uint32_t)page_bytes;
+  // Buffer loads need the pool within 32-bit offsets and 24-bit page numbers
+  // and page sizes for the multiply.
+  const bool buf = num_pages < (1 << 24) && page_bytes < (1 << 24) &&
+                   num_pages * page_bytes <= (int64_t)INT32_MAX;
+  p.pool_bytes = buf ? (uint32_t)(num_pages * page_bytes) : 0u;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (head_dim == 64) {

@@ -242,3 +242,33 @@ def test_prefill_long_prefixes(prefix):
     out = run_prefill(w)
     torch.cuda.synchronize()
     print(pages, assert_close(f64(out), ref, f"long prefixes, {pages} pages"))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_pool_beyond_2gib(d):
+    # Pools of up to 2 GiB are read with buffer loads at 32-bit offsets,
+    # larger ones with 64-bit addresses.  The same batch, its pages moved to
+    # the far end of a 2.46 GB pool, gives the same bits as in its own small
+    # pool, and stays within tolerance of the oracle.
+    hq, hkv, ps = 8, 2, 16
+    w = inputs.build_prefill(2, hq, hkv, d, ps, [100, 37], [70, 130], seed=97 + d, device="cuda")
+    ref = _oracle(w)
+    run_store(w)
+    small = run_prefill(w).clone()
+    page_bytes = ps * hkv * d * 2
+    big_pages = (2**31 + 2**29) // page_bytes
+    n_small = w.k_cache.shape[0]
+    shift = big_pages - n_small
+    kb = torch.empty((big_pages, ps, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vb = torch.empty_like(kb)
+    kb[shift:].copy_(w.k_cache)
+    vb[shift:].copy_(w.v_cache)
+    table = (w.page_table + shift).contiguous()
+    print(f"prefill pool beyond 2 GiB: d={d} pages={big_pages} shift={shift}", flush=True)
+    big = pkv.pkv_paged_attn_prefill(w.q, w.cu_seqlens_q, w.prefix_lens, w.max_q_len,
+                                     w.max_seq_len, kb, vb, table, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(big.view(torch.int16), small.view(torch.int16))
+    print(d, assert_close(f64(big), ref, "pool beyond 2 GiB"))
+    del kb, vb
+    torch.cuda.empty_cache()
