@@ -23,8 +23,9 @@
 //
 // Per 64-key tile:
 //   * K and V rows are fetched through the page table into registers three
-//     tiles ahead and written to LDS (row-major) one tile ahead, while the
-//     step's QK^T MFMAs run.
+//     tiles ahead (buffer loads at 32-bit offsets when a pool is at most
+//     2 GiB) and written to LDS (row-major) one tile ahead, while the step's
+//     QK^T MFMAs run.
 //   * S^T = K Q^T with MFMA 32x32x16 bf16 (A = K from LDS, B = Q resident in
 //     registers); lane l owns column l % 32, 32 keys of it per 32x32 block.
 //   * Online softmax per column in base 2.  The first tile sets the
