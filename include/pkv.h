@@ -30,10 +30,11 @@
  * - Errors: a non-zero status is returned BEFORE anything is enqueued when
  *   an argument the host can check is wrong; PKV_EHIP reports a launch
  *   failure.  Device-resident values (page ids, slots, lengths) are not
- *   checked on the host: out-of-range values are clamped, skipped or (with
- *   range-checked buffer loads) read as zeros inside the kernels, so no
- *   access leaves the buffers described here, and the affected outputs are
- *   unspecified.
+ *   checked on the host: out-of-range values are clamped or skipped inside
+ *   the kernels; where rows are fetched by range-checked buffer loads, a
+ *   page id outside the pool reads zeros or (ids of 2^24 and more, whose
+ *   offset wraps) other rows of the same pool.  No access leaves the buffers
+ *   described here, and the affected outputs are unspecified.
  * - Thread safety: calls may be made from any host thread; calls that share
  *   an output or workspace buffer must be ordered by the caller.
  */

@@ -123,8 +123,10 @@ __device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int 
 
 // BUF: the pools are below 4 GiB and their pages and page numbers below 2^24,
 // so rows are fetched by buffer loads at 32-bit offsets from the pool bases
-// (one 24-bit multiply-add per row instead of 64-bit address arithmetic;
-// offsets past the pool read zeros).
+// (one 24-bit multiply-add per row instead of 64-bit address arithmetic).
+// A page id outside the pool is not clamped on this path: its offset, taken
+// modulo 2^32 from the id's low 24 bits, either lies past the pool, where
+// the load's range check returns zeros, or on other rows of the same pool.
 template <int D, int NB, int G, bool BUF>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   constexpr int QT = 128 * NB / G;
@@ -341,8 +343,8 @@ __device__ __forceinline__ bool attend_item(const PrefillParams& p, int qt, int 
     }
   };
   // Register set `set` (a constant at every call) holds the rows of tile kt.
-  // Page numbers at or past num_pages read the last page (never unowned
-  // memory; such a table is invalid input).
+  // With 64-bit addresses, page numbers at or past num_pages read the last
+  // page (never unowned memory; such a table is invalid input).
   auto fetch_rows = [&](int kt, auto set_c) {
     constexpr int set = decltype(set_c)::value;
     if (whole(kt)) {
