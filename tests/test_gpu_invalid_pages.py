@@ -1,11 +1,18 @@
-"""Page tables with out-of-range entries inside some requests' used pages:
+"""Device-resident values that the host cannot check, out of range.
+
+Page tables get out-of-range entries inside some requests' used pages:
 negative ids, ids at and past the pool's page count, ids beyond 2^24 and
-INT32_MAX.  No page id is checked on the host.  The kernels keep every
-access inside the pools: decode windows read page 0 for such ids, the
-prefill and prefix-pass fetches clamp them to the last page, and the prefill's
-buffer loads at 32-bit offsets read zeros past the pool.  The other
-requests' outputs are unchanged bit for bit, and the pools are unchanged.
-What a request with such a page gets is unspecified and not compared."""
+INT32_MAX.  The kernels keep every access inside the pools.  Decode windows
+read page 0 for such ids.  The prefill and prefix-pass fetches clamp them to
+the last page.  The prefill's buffer loads at 32-bit offsets read zeros past
+the pool.
+
+Lengths get values beyond max_seq_len and below zero; the kernels clamp
+them to [0, max_seq_len].
+
+In every case the other requests' outputs are unchanged bit for bit, and the
+pools are unchanged.  What an affected request gets is unspecified and not
+compared."""
 
 import numpy as np
 import pytest
@@ -167,3 +174,41 @@ def test_prefill_invalid_page_ids_pool_beyond_2gib():
     assert torch.equal(kb[shift:].view(torch.int16), w.k_cache.view(torch.int16))
     del kb, vb
     torch.cuda.empty_cache()
+
+
+def test_decode_lengths_beyond_max_seq_len():
+    # Lengths above max_seq_len read max_seq_len tokens; with a fixed split
+    # every other request keeps its splits and its bits.
+    B, hq, hkv, d, ps = 24, 32, 8, 64, 16
+    lens = np.random.default_rng(61).integers(100, 1500, size=B).astype(np.int32)
+    w = inputs.build_decode(B, hq, hkv, d, ps, lens, seed=67, device="cuda")
+    print("out-of-range lengths, decode", flush=True)
+
+    def call(seq_lens):
+        return pkv.pkv_paged_attn_decode(w.q, w.k_cache, w.v_cache, w.page_table, seq_lens,
+                                         w.max_seq_len, w.scale, split_tokens=256)
+
+    clean = call(w.seq_lens).clone()
+    bad = w.seq_lens.clone()
+    bad[5] = w.max_seq_len + 999
+    bad[9] = 2**31 - 1
+    got = call(bad)
+    torch.cuda.synchronize()
+    _same_rows(got, clean, [r for r in range(B) if r not in (5, 9)], "decode lengths")
+
+
+def test_prefill_prefix_lengths_out_of_range():
+    # A prefix beyond max_seq_len - (new tokens) is cut to it and a negative
+    # one read as 0; the other requests keep their bits.
+    hq, hkv, d, ps = 8, 2, 64, 16
+    prefix, qlens = [100, 300, 0, 50], [70, 130, 40, 200]
+    w = inputs.build_prefill(4, hq, hkv, d, ps, prefix, qlens, seed=71, device="cuda")
+    run_store(w)
+    clean = run_prefill(w).clone()
+    w.prefix_lens = w.prefix_lens.clone()
+    w.prefix_lens[0] = 2**31 - 1  # read as 430 - 70 keys before its new tokens
+    w.prefix_lens[3] = -5
+    print("out-of-range prefix lengths, prefill", flush=True)
+    got = run_prefill(w)
+    torch.cuda.synchronize()
+    _same_rows(got, clean, _prefill_rows(w, [1, 2]), "prefill prefix lengths")
