@@ -16,9 +16,9 @@ from gpu_helpers import assert_close, f64, host_pools, run_decode, run_prefill, 
 
 pytestmark = pytest.mark.gpu
 
-N_DECODE = 96
-N_MULTI = 48
-N_PREFILL = 40
+N_DECODE = 192
+N_MULTI = 96
+N_PREFILL = 80
 
 
 def _heads(rng):
@@ -139,8 +139,8 @@ def test_random_prefill(i):
     print(i, assert_close(f64(out), ref, f"random prefill {i}"))
 
 
-N_SHARED = 16
-N_LARGE = 8
+N_SHARED = 32
+N_LARGE = 16
 
 
 def _shared_case(i):
