@@ -46,17 +46,24 @@ struct DecodeMetaParams {
 __device__ __forceinline__ int new_tokens(const PrefillMetaParams& p, int r) {
   const int n = p.seq_lens[r];
   const int c = max(p.prefix_lens[r], 0);
-  return max(n - c, 0);
+  return (int)max((int64_t)n - c, (int64_t)0);
 }
 
 // Slot of logical position t of a request, or -1 when the position falls
 // outside the page-table row.  Only page ids are read; the pool is not.
 __device__ __forceinline__ int32_t slot_of(const int32_t* row, int pt_stride, int page_size,
-                                           int t) {
-  const int i = t / page_size;
+                                           int64_t t) {
+  const int64_t i = t / page_size;
   if (t < 0 || i >= pt_stride) return -1;
   const int64_t s = (int64_t)row[i] * page_size + t % page_size;
   return (s < 0 || s > INT32_MAX) ? -1 : (int32_t)s;
+}
+
+// Sum of two token counts, both >= 0, saturated at INT32_MAX: lengths are
+// device values the host does not check, and saturated prefix sums stay
+// non-negative and non-decreasing however large they are.
+__device__ __forceinline__ int sat_add(int a, int b) {
+  return (int)min((int64_t)a + b, (int64_t)INT32_MAX);
 }
 
 // cu_seqlens by one workgroup: the requests go in chunks of 1024, each
@@ -75,13 +82,13 @@ __global__ __launch_bounds__(kScanThreads) void prefill_cu_kernel(PrefillMetaPar
     buf[0][tid] = r < p.num_seqs ? new_tokens(p, r) : 0;
     __syncthreads();
     for (int off = 1; off < kScanThreads; off <<= 1) {
-      const int v = buf[cur][tid] + (tid >= off ? buf[cur][tid - off] : 0);
+      const int v = sat_add(buf[cur][tid], tid >= off ? buf[cur][tid - off] : 0);
       buf[cur ^ 1][tid] = v;
       cur ^= 1;
       __syncthreads();
     }
-    if (r < p.num_seqs) p.cu_seqlens[r + 1] = carry + buf[cur][tid];
-    carry += buf[cur][kScanThreads - 1];
+    if (r < p.num_seqs) p.cu_seqlens[r + 1] = sat_add(carry, buf[cur][tid]);
+    carry = sat_add(carry, buf[cur][kScanThreads - 1]);
     __syncthreads();  // every thread has read the chunk total before the next chunk
   }
 }
@@ -105,26 +112,29 @@ __global__ __launch_bounds__(kScanThreads) void prefill_meta_small_kernel(Prefil
   buf[0][tid] = cnt;
   __syncthreads();
   for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = buf[cur][tid] + (tid >= off ? buf[cur][tid - off] : 0);
+    const int v = sat_add(buf[cur][tid], tid >= off ? buf[cur][tid - off] : 0);
     buf[cur ^ 1][tid] = v;
     cur ^= 1;
     __syncthreads();
   }
-  const int* end = buf[cur];  // end[q]: new tokens of requests 0..q
+  // end[q]: new tokens of requests 0..q (saturated), non-decreasing, so for
+  // t < end[num_seqs - 1] the search below lands on a request of the batch
+  const int* end = buf[cur];
   if (blockIdx.x == 0) {
     if (tid == 0) p.cu_seqlens[0] = 0;
     if (r < p.num_seqs) p.cu_seqlens[r + 1] = end[tid];
   }
   const int total = min(end[kScanThreads - 1], p.max_tokens);
-  for (int t = blockIdx.x * kScanThreads + tid; t < total; t += gridDim.x * kScanThreads) {
+  for (int64_t t = blockIdx.x * kScanThreads + tid; t < total; t += gridDim.x * kScanThreads) {
     // the first request whose end offset exceeds t
     int q = 0;
 #pragma unroll
     for (int step = kScanThreads / 2; step >= 1; step >>= 1)
       if (end[q + step - 1] <= t) q += step;
+    q = min(q, p.num_seqs - 1);
     const int start = q == 0 ? 0 : end[q - 1];
     const int32_t* row = p.page_table + (int64_t)q * p.pt_stride;
-    p.out_loc[t] = slot_of(row, p.pt_stride, p.page_size, first_pos[q] + (t - start));
+    p.out_loc[t] = slot_of(row, p.pt_stride, p.page_size, (int64_t)first_pos[q] + (t - start));
   }
 }
 
@@ -134,15 +144,14 @@ __global__ __launch_bounds__(kScanThreads) void prefill_meta_small_kernel(Prefil
 __global__ __launch_bounds__(256) void prefill_slots_kernel(PrefillMetaParams p) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int start = p.cu_seqlens[r];
+  const int start = p.cu_seqlens[r];  // >= 0: saturated sums
   const int len = new_tokens(p, r);
+  if (start < 0) return;
   const int32_t* row = p.page_table + (int64_t)r * p.pt_stride;
   const int first = max(p.prefix_lens[r], 0);
-  for (int i = tid; i < len; i += 256) {
-    const int t = start + i;
-    if (t >= p.max_tokens) break;
-    p.out_loc[t] = slot_of(row, p.pt_stride, p.page_size, first + i);
-  }
+  const int n = min(len, p.max_tokens - start);  // tokens that land inside out_loc
+  for (int64_t i = tid; i < n; i += 256)
+    p.out_loc[start + i] = slot_of(row, p.pt_stride, p.page_size, first + i);
 }
 
 __global__ __launch_bounds__(256) void decode_meta_kernel(DecodeMetaParams p) {

@@ -69,3 +69,43 @@ def test_metadata_feeds_the_workloads():
     out_loc = pkv.pkv_decode_metadata(w.seq_lens, w.page_table, w.page_size)
     torch.cuda.synchronize()
     assert torch.equal(out_loc, w.out_loc)
+
+
+@pytest.mark.parametrize("B", [5, 1100])  # the one-launch builder and the chunked scan
+def test_prefill_metadata_huge_lengths(B):
+    """Lengths near INT32_MAX (device values the host does not check): the
+    counts are summed with saturation, so cu_seqlens stays non-negative and
+    non-decreasing, every slot written lies below max_tokens, and the tokens
+    before the first huge request (and that request's first ones) get their
+    exact slots."""
+    rng = np.random.default_rng(91 + B)
+    ps, width = 16, 6
+    table = _table(rng, B, width, B * width + 20)
+    seq = rng.integers(0, width * ps + 1, size=B).astype(np.int32)
+    pre = np.zeros(B, np.int32)
+    big = [1, 2] if B == 5 else [600, 1050]
+    seq[big[0]] = 2**31 - 1
+    seq[big[1]] = 2**31 - 1
+    pre[big[1]] = 10
+    if B == 5:
+        seq[4], pre[4] = -2**31, 2**31 - 1  # no new token
+    head = big[0]  # requests before the first huge one are exact
+    cu_head, slots_head = orc.prefill_metadata(seq[:head], pre[:head], table[:head], ps)
+    start = int(cu_head[-1])
+    cap = start + 100
+    # the first 100 tokens of the huge request, at positions 0..99 of its row
+    slots_big = [orc.slot_of(table[head], t, ps) for t in range(100)]
+    dev = lambda a: torch.from_numpy(a).cuda()
+    out_loc = torch.full((cap + 8,), -7, dtype=torch.int32, device="cuda")
+    print(f"huge lengths: B={B} huge requests {big} max_tokens {cap}", flush=True)
+    cu, out_loc = pkv.pkv_prefill_metadata(dev(seq), dev(pre), dev(table), ps, cap,
+                                           out_loc=out_loc)
+    torch.cuda.synchronize()
+    cu = cu.cpu().numpy().astype(np.int64)
+    got = out_loc.cpu().numpy()
+    assert np.array_equal(cu[:head + 1], cu_head)
+    assert (cu >= 0).all() and (np.diff(cu) >= 0).all()
+    assert cu[head + 1] == 2**31 - 1  # saturated from the first huge count on
+    assert np.array_equal(got[:start], slots_head)
+    assert np.array_equal(got[start:cap], np.array(slots_big, np.int32))
+    assert (got[cap:] == -7).all(), "entries past max_tokens must not be written"
