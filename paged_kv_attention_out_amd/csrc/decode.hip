@@ -103,12 +103,14 @@ struct DecodeParams {
   // after them.  Null: no request skips anything.
   const int32_t* skip;
   int32_t ksplit;
+  int32_t max_skip;  // max_shared_len: the pass's slots are sized for at most this many
 };
 
 // Tokens of request r attended by the shared-prefix pass (0 without one),
-// a multiple of 16 not above n, and the partial slots that pass fills.
+// a multiple of 16 above neither n nor max_shared_len, and the partial slots
+// that pass fills.
 __device__ __forceinline__ int skip_tokens(const DecodeParams& p, int skip_raw, int n) {
-  return p.skip == nullptr ? 0 : min(max(skip_raw, 0), max(n, 0)) & ~15;
+  return p.skip == nullptr ? 0 : min(max(skip_raw, 0), min(max(n, 0), p.max_skip)) & ~15;
 }
 __device__ __forceinline__ int prefix_slots(const DecodeParams& p, int skip) {
   return skip == 0 ? 0 : (skip + p.ksplit - 1) / p.ksplit;
@@ -1459,6 +1461,10 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const int32
     // shared-prefix batch.)
     p.skip = groups->shared_lens;
     p.ksplit = pkv_prefix::kSplit;
+    // A shared length above max_shared_len (a device value, not checked on
+    // the host) is cut to it, so a request's partial slots stay among the
+    // nks + nsm sized above.
+    p.max_skip = groups->max_shared_len;
     if (nks > 0) {
       const int nb = head_dim == 64 ? 2 : 1;
       const int qtile = 128 * nb / g;

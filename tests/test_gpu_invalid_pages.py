@@ -212,3 +212,37 @@ def test_prefill_prefix_lengths_out_of_range():
     got = run_prefill(w)
     torch.cuda.synchronize()
     _same_rows(got, clean, _prefill_rows(w, [1, 2]), "prefill prefix lengths")
+
+
+def test_decode_shared_lengths_out_of_range():
+    # Shared lengths above max_shared_len or below zero are cut to
+    # [0, max_shared_len]: each request's partials stay inside the workspace
+    # sized for max_shared_len (a guard after it stays untouched), and the
+    # requests with valid lengths keep their bits.
+    from test_gpu_decode_shared import _grouped
+    hq, hkv, d, ps = 32, 8, 64, 16
+    groups = [(6, 300), (5, 500), (4, 0)]
+    w, cu, shared, max_group, max_shared = _grouped(hq, hkv, d, ps, groups, 73, False)
+    B = w.num_seqs
+    need = pkv.pkv_paged_attn_decode_shared_workspace_bytes(B, hq, hkv, d, w.max_seq_len,
+                                                            max_shared, 256)
+    guard = 1 << 20
+    ws = torch.full((need + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+
+    def call(sh):
+        return pkv.pkv_paged_attn_decode_shared(
+            w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens, w.max_seq_len, cu, sh,
+            max_group, max_shared, w.scale, workspace=ws[:need], split_tokens=256)
+
+    clean = call(shared).clone()
+    bad = shared.clone()
+    bad[6] = 2**31 - 1   # the first member of group 1: its pass reads max_shared_len
+    bad[12] = 2**31 - 1  # group 2 shares nothing; these two claim more
+    bad[14] = 2**31 - 1
+    bad[13] = -5
+    print(f"out-of-range shared lengths: groups {groups}, workspace {need} bytes", flush=True)
+    got = call(bad)
+    torch.cuda.synchronize()
+    affected = set(range(6, 11)) | {12, 13, 14}
+    _same_rows(got, clean, [r for r in range(B) if r not in affected], "shared lengths")
+    assert (ws[need:] == 0x5A).all(), "a partial landed past the workspace"
