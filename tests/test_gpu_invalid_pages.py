@@ -5,10 +5,12 @@ negative ids, ids at and past the pool's page count, ids beyond 2^24 and
 INT32_MAX.  The kernels keep every access inside the pools.  Decode windows
 read page 0 for such ids.  The prefill and prefix-pass fetches clamp them to
 the last page.  The prefill's buffer loads at 32-bit offsets read zeros past
-the pool.
+the pool, or other rows of the pool for ids of 2^24 and more (their offsets
+wrap).
 
 Lengths get values beyond max_seq_len and below zero; the kernels clamp
-them to [0, max_seq_len].
+them to [0, max_seq_len].  Shared-prefix lengths are cut to
+[0, max_shared_len].
 
 In every case the other requests' outputs are unchanged bit for bit, and the
 pools are unchanged.  What an affected request gets is unspecified and not
