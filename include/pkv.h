@@ -245,7 +245,7 @@ size_t pkv_decode_step_noalloc_max_bytes(void);
  * out_loc are given), up to rounding.  The work is split in two passes on
  * `stream`: for every group, the queries of all its members (all query
  * heads of a KV head) against the group's shared prefix as one MFMA
- * product per 64-key split of the prefix; then every request's remaining
+ * product per 128-key split of the prefix; then every request's remaining
  * tokens as in pkv_paged_attn_decode; the partial results of both are
  * merged by the split-merge kernel.
  *
